@@ -1,0 +1,183 @@
+"""Bench: FP32 GEMM throughput (2MNK/s) on one MI355X, through the C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one C = A x B call of the planner's plan (every kernel it launches,
+split-K reduce included) on inputs already resident in HBM. W untimed steps,
+then K timed steps between two device synchronisations; one JSON line on
+stdout. Each call is also bracketed by a HIP event pair on the stream it is
+launched on, which gives the per-launch duration used for the roofline.
+
+The CPU baseline is the oracle (plain FP64 triple loop) run on the host's
+cores on a bounded slab of rows of the same product, scaled to TFLOP/s; the
+same rows of the GPU result are compared with it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import gemm_inputs  # noqa: E402
+from fp32_gemm_07_amd import binding, roofline  # noqa: E402
+
+METRIC = "FP32 GEMM TFLOPS (2MNK/s) and % of MI355X FP32 peak, 1 GPU"
+DEFAULT_WORKLOAD = "square_4096"
+
+# HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+# keyed by (workload, kernel name of the plan); scaled by the copy-kernel
+# calibration factor. None until measured for the current kernel build.
+MEASURED_TRAFFIC_BYTES = {}
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in gemm_inputs.WORKLOADS])
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the oracle's CPU-baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args(argv)
+
+
+def cpu_baseline(A, B, C_gpu, target_s: float):
+    """Time the oracle on a slab of rows of the same product (bounded to about
+    target_s seconds of host time); compare those rows with the GPU result."""
+    import oracle
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build(force=True)
+    M, K = A.shape
+    N = B.shape[1]
+    threads = oracle.num_threads()
+    # calibrate on a few rows, then size the slab
+    r0 = min(M, 4 * max(1, threads))
+    t0 = time.perf_counter()
+    oracle.gemm(A[:r0], B)
+    dt0 = max(time.perf_counter() - t0, 1e-6)
+    rows = int(min(M, max(r0, r0 * target_s / dt0)))
+    rows = max(threads, (rows // threads) * threads) if rows >= threads else rows
+    rows = min(rows, M)
+    t0 = time.perf_counter()
+    C_ref, S = oracle.gemm(A[:rows], B)
+    dt = time.perf_counter() - t0
+    flops = roofline.gemm_flops(rows, N, K)
+    err = np.abs(C_gpu[:rows].astype(np.float64) - C_ref)
+    ratio = float(np.max(err / (1e-5 * S + 1e-6))) if err.size else 0.0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of C ({rows} x {N} outputs, full K = {K}), "
+                  f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, FP64 accumulation",
+        "seconds": dt,
+        "sample_parity_worst_ratio": ratio,
+    }
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "a multi-GPU run is not part of it.", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    w = gemm_inputs.BY_NAME[args.workload]
+    M, N, K = w.M, w.N, w.K
+    plan = binding.gemm_f32_plan(M, N, K)
+    kname = binding.gemm_kernel_name(plan.kernel)
+
+    A, B = gemm_inputs.draw_workload(w)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    ws_bytes = binding.gemm_f32_workspace_bytes(M, N, K)
+    ws = torch.empty((max(ws_bytes // 4, 1),), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+
+    def step():
+        binding.gemm_f32_ex(dA, dB, dC, M, N, K, ws, ws_bytes, h)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    flops = roofline.gemm_flops(M, N, K)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (launch_ms.mean() * 1e-3) / 1e12
+    peak = roofline.PEAK_FP32_MFMA_TFLOPS
+    props = torch.cuda.get_device_properties(0)
+
+    C = dC.cpu().numpy()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "M": M, "N": N, "K": K, "dist": w.dist, "seed": w.seed,
+            "plan": {"kernel": kname, "split_k": plan.split_k, "k_chunk": plan.k_chunk},
+            "parallelism": "1 GPU",
+        },
+        "pct_of_fp32_peak": round(100 * value / peak, 2),
+        "launch_ms": {"mean": round(float(launch_ms.mean()), 4),
+                      "median": round(float(np.median(launch_ms)), 4),
+                      "min": round(float(launch_ms.min()), 4)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": MEASURED_TRAFFIC_BYTES.get((w.name, kname)),
+            "algorithmic_flop_per_launch": flops,
+            "compulsory_bytes_per_launch": roofline.compulsory_bytes(M, N, K),
+            "kernel": kname,
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+        "output_finite": bool(np.isfinite(C).all()),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(A, B, C, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

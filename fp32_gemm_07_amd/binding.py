@@ -1,0 +1,170 @@
+"""ctypes binding of libgemm (the C ABI in include/gemm.h), same names, marshalling only.
+
+Every entry takes device pointers as Python ints (or anything with a
+``data_ptr()`` method, such as a torch tensor on the GPU) and a HIP stream
+handle as an int (``torch.cuda.current_stream().cuda_stream``; 0 = null
+stream). Nonzero statuses raise ``GemmError``; nothing here computes.
+
+The library must have been built (``fp32_gemm_07_amd.build.build()``): a
+missing library raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_DIM = 1
+GEMM_ERR_NULL_PTR = 2
+GEMM_ERR_ALIAS = 3
+GEMM_ERR_WORKSPACE = 4
+GEMM_ERR_INVALID_PLAN = 5
+GEMM_ERR_HIP = 6
+GEMM_ERR_UNSUPPORTED_DEVICE = 7
+
+GEMM_KERNEL_AUTO = 0
+GEMM_KERNEL_MFMA_256x256 = 1
+GEMM_KERNEL_MFMA_256x128 = 2
+GEMM_KERNEL_MFMA_128x128 = 3
+GEMM_KERNEL_MFMA_64x64 = 4
+GEMM_KERNEL_VALU_64x64 = 10
+
+KERNELS = {
+    "mfma_256x256": GEMM_KERNEL_MFMA_256x256,
+    "mfma_256x128": GEMM_KERNEL_MFMA_256x128,
+    "mfma_128x128": GEMM_KERNEL_MFMA_128x128,
+    "mfma_64x64": GEMM_KERNEL_MFMA_64x64,
+    "valu_64x64": GEMM_KERNEL_VALU_64x64,
+}
+
+# Every symbol include/gemm.h declares.
+EXPORTS = (
+    "gemm_f32", "gemm_f32_workspace_bytes", "gemm_f32_ex", "gemm_f32_plan",
+    "gemm_f32_plan_workspace_bytes", "gemm_f32_with_plan", "gemm_kernel_name",
+    "gemm_status_string", "gemm_last_hip_error",
+)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        text = gemm_status_string(status)
+        if status == GEMM_ERR_HIP:
+            text += f" (hipError_t {gemm_last_hip_error()})"
+        super().__init__(f"{where}: {text} [status {status}]")
+
+
+class gemm_plan_t(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("k_chunk", ctypes.c_int), ("reserved", ctypes.c_int)]
+
+    def __repr__(self):
+        return (f"gemm_plan_t(kernel={gemm_kernel_name(self.kernel)}, split_k={self.split_k}, "
+                f"k_chunk={self.k_chunk})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load libgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgemm is not built ({LIB_PATH} missing); run "
+                               "fp32_gemm_07_amd.build.build() first")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        plan_p = ctypes.POINTER(gemm_plan_t)
+        lib.gemm_f32.argtypes = [vp, vp, vp, i, i, i, vp]
+        lib.gemm_f32.restype = i
+        lib.gemm_f32_workspace_bytes.argtypes = [i, i, i]
+        lib.gemm_f32_workspace_bytes.restype = sz
+        lib.gemm_f32_ex.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
+        lib.gemm_f32_ex.restype = i
+        lib.gemm_f32_plan.argtypes = [i, i, i, plan_p]
+        lib.gemm_f32_plan.restype = i
+        lib.gemm_f32_plan_workspace_bytes.argtypes = [i, i, i, plan_p]
+        lib.gemm_f32_plan_workspace_bytes.restype = sz
+        lib.gemm_f32_with_plan.argtypes = [vp, vp, vp, i, i, i, plan_p, vp, sz, vp]
+        lib.gemm_f32_with_plan.restype = i
+        lib.gemm_kernel_name.argtypes = [i]
+        lib.gemm_kernel_name.restype = ctypes.c_char_p
+        lib.gemm_status_string.argtypes = [i]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_last_hip_error.argtypes = []
+        lib.gemm_last_hip_error.restype = i
+        _lib = lib
+    return _lib
+
+
+def _addr(p) -> int:
+    if p is None:
+        return 0
+    if hasattr(p, "data_ptr"):
+        return int(p.data_ptr())
+    return int(p)
+
+
+def _check(status: int, where: str) -> int:
+    if status != GEMM_OK:
+        raise GemmError(status, where)
+    return status
+
+
+def gemm_f32(A, B, C, M: int, N: int, K: int, stream: int = 0) -> None:
+    _check(load().gemm_f32(_addr(A), _addr(B), _addr(C), M, N, K, stream or None), "gemm_f32")
+
+
+def gemm_f32_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load().gemm_f32_workspace_bytes(M, N, K))
+
+
+def gemm_f32_ex(A, B, C, M: int, N: int, K: int, workspace, workspace_bytes: int,
+                stream: int = 0) -> None:
+    _check(load().gemm_f32_ex(_addr(A), _addr(B), _addr(C), M, N, K, _addr(workspace) or None,
+                              workspace_bytes, stream or None), "gemm_f32_ex")
+
+
+def gemm_f32_plan(M: int, N: int, K: int) -> gemm_plan_t:
+    p = gemm_plan_t()
+    _check(load().gemm_f32_plan(M, N, K, ctypes.byref(p)), "gemm_f32_plan")
+    return p
+
+
+def make_plan(kernel: int, split_k: int = 1) -> gemm_plan_t:
+    return gemm_plan_t(kernel, split_k, 0, 0)
+
+
+def gemm_f32_plan_workspace_bytes(M: int, N: int, K: int, plan: gemm_plan_t) -> int:
+    return int(load().gemm_f32_plan_workspace_bytes(M, N, K, ctypes.byref(plan)))
+
+
+def gemm_f32_with_plan(A, B, C, M: int, N: int, K: int, plan: gemm_plan_t, workspace=None,
+                       workspace_bytes: int = 0, stream: int = 0) -> None:
+    _check(load().gemm_f32_with_plan(_addr(A), _addr(B), _addr(C), M, N, K, ctypes.byref(plan),
+                                     _addr(workspace) or None, workspace_bytes, stream or None),
+           "gemm_f32_with_plan")
+
+
+def gemm_kernel_name(kernel: int) -> str:
+    return load().gemm_kernel_name(kernel).decode()
+
+
+def gemm_status_string(status: int) -> str:
+    return load().gemm_status_string(status).decode()
+
+
+def gemm_last_hip_error() -> int:
+    return int(load().gemm_last_hip_error())
+
+
+def raw_status(fn: str, *args) -> int:
+    """Call an entry point and return its raw status (for tests of the error paths)."""
+    return int(getattr(load(), fn)(*args))

@@ -1,0 +1,384 @@
+// Host side of libgemm: argument checks, planner, workspace, launches.
+// The C ABI is declared (and documented) in include/gemm.h.
+#include "gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "gemm_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return GEMM_ERR_HIP;
+}
+
+constexpr int kNumCus = 256;
+
+// ---------------------------------------------------------------------------
+// Kernel configurations.
+struct KernelInfo {
+  int id;
+  int bm, bn, bk;
+  const char *name;
+};
+
+constexpr KernelInfo kKernels[] = {
+    {GEMM_KERNEL_MFMA_256x256, 256, 256, 16, "mfma_f32_256x256x16"},
+    {GEMM_KERNEL_MFMA_256x128, 256, 128, 16, "mfma_f32_256x128x16"},
+    {GEMM_KERNEL_MFMA_128x128, 128, 128, 16, "mfma_f32_128x128x16"},
+    {GEMM_KERNEL_MFMA_64x64, 64, 64, 16, "mfma_f32_64x64x16"},
+    {GEMM_KERNEL_VALU_64x64, 64, 64, 16, "valu_f32_64x64x16"},
+};
+
+const KernelInfo *find_kernel(int id) {
+  for (const auto &k : kKernels)
+    if (k.id == id) return &k;
+  return nullptr;
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+struct Resolved {
+  const KernelInfo *k;
+  int splits;     // number of K ranges actually launched (>= 1)
+  int k_chunk;    // length of each K range
+  long long tiles_m, tiles_n;
+};
+
+// Turn (kernel, requested split) into launch geometry. The split is clamped
+// to the number of K steps; every range then holds at least one element.
+bool resolve(int M, int N, int K, int kernel, int split_req, Resolved *out) {
+  const KernelInfo *k = find_kernel(kernel);
+  if (!k || split_req < 1) return false;
+  out->k = k;
+  out->tiles_m = ceil_div(M, k->bm);
+  out->tiles_n = ceil_div(N, k->bn);
+  const long long ksteps = std::max<long long>(1, ceil_div(K, k->bk));
+  const long long s = std::min<long long>(split_req, ksteps);
+  const long long chunk = ceil_div(ceil_div(std::max(K, 1), s), k->bk) * k->bk;
+  out->k_chunk = static_cast<int>(std::min<long long>(chunk, INT_MAX));
+  out->splits = static_cast<int>(K > 0 ? ceil_div(K, out->k_chunk) : 1);
+  return true;
+}
+
+size_t workspace_for(int M, int N, const Resolved &r) {
+  return r.splits > 1 ? sizeof(float) * (size_t)r.splits * (size_t)M * (size_t)N : 0;
+}
+
+// The planner. Rules of thumb for one MI355X (256 CUs):
+//  - enough 256x256 tiles to give every CU one (>= 192): 256x256, no split;
+//  - few output tiles but a long K: 256x256 (or 128x128 for narrow outputs)
+//    split along K until about 256 workgroups, keeping each K range >= 1024;
+//  - otherwise the smallest MFMA tile that still gives about one workgroup
+//    per CU.
+void plan(int M, int N, int K, int *kernel, int *split) {
+  *split = 1;
+  const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
+  const long long t128 = ceil_div(M, 128) * ceil_div(N, 128);
+  const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
+  if (t256 >= 192) {
+    *kernel = GEMM_KERNEL_MFMA_256x256;
+    return;
+  }
+  // Long-K shapes: split K.
+  const long long kmin = 1024;
+  if (K >= 4 * kmin) {
+    const bool wide = M >= 256 && N >= 256;
+    const long long tiles = wide ? t256 : t128;
+    long long s = std::max<long long>(1, kNumCus / std::max<long long>(1, tiles));
+    s = std::min<long long>(s, K / kmin);
+    if (s > 1 || tiles >= 96) {
+      *kernel = wide ? GEMM_KERNEL_MFMA_256x256 : GEMM_KERNEL_MFMA_128x128;
+      *split = static_cast<int>(s);
+      return;
+    }
+  }
+  if (t128 >= 192) {
+    *kernel = GEMM_KERNEL_MFMA_128x128;
+    return;
+  }
+  (void)t64;
+  *kernel = GEMM_KERNEL_MFMA_64x64;
+}
+
+// ---------------------------------------------------------------------------
+// Device check (once per device): the code objects are built for gfx950 only.
+std::mutex g_mu;
+constexpr int kMaxDevices = 64;
+int g_dev_ok[kMaxDevices];            // 0 unknown, 1 gfx950, -1 other
+void *g_ws[kMaxDevices];
+size_t g_ws_bytes[kMaxDevices];
+
+int check_device(int *dev_out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+  }
+  return g_dev_ok[dev] == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks (no HIP calls).
+bool overlaps(const void *p, size_t pb, const void *q, size_t qb) {
+  if (!pb || !qb) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + pb;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + qb;
+  return a0 < b1 && b0 < a1;
+}
+
+int validate(const float *A, const float *B, const float *C, int M, int N, int K) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_DIM;
+  // Tile and workgroup counts are kept in int on the device.
+  if ((long long)M * N > (1LL << 40) || (long long)M * K > (1LL << 40) ||
+      (long long)K * N > (1LL << 40))
+    return GEMM_ERR_INVALID_DIM;
+  // An operand is touched only when there is an output to produce (M, N > 0),
+  // and A and B only when the sum is not empty (K > 0).
+  const bool any_out = M > 0 && N > 0;
+  const size_t a_bytes = any_out ? sizeof(float) * (size_t)M * (size_t)K : 0;
+  const size_t b_bytes = any_out ? sizeof(float) * (size_t)K * (size_t)N : 0;
+  const size_t c_bytes = any_out ? sizeof(float) * (size_t)M * (size_t)N : 0;
+  if ((a_bytes && !A) || (b_bytes && !B) || (c_bytes && !C)) return GEMM_ERR_NULL_PTR;
+  if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)) return GEMM_ERR_ALIAS;
+  return GEMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch helpers.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES, int VA, int VB, bool CHECK>
+void launch_mfma_t(const float *A, const float *B, float *out, int M, int N, int K,
+                   const Resolved &r, long long slab, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
+  hipLaunchKernelGGL((gemm::mfma_gemm_kernel<BM, BN, 16, WAVES_M, WAVES_N, VA, VB, CHECK, MIN_WAVES>),
+                     grid, dim3(gemm::kThreads), 0, stream, A, B, out, M, N, K, r.k_chunk,
+                     static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits, slab);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES>
+void launch_mfma(const float *A, const float *B, float *out, int M, int N, int K,
+                 const Resolved &r, long long slab, hipStream_t stream) {
+  const bool va = (K % 4 == 0) && (reinterpret_cast<uintptr_t>(A) % 16 == 0);
+  const bool vb = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(B) % 16 == 0);
+  const bool exact = (M % BM == 0) && (N % BN == 0) && (K % 16 == 0) && (r.k_chunk % 16 == 0);
+#define LGEMM_CASE(VA_, VB_, CK_) \
+  launch_mfma_t<BM, BN, WAVES_M, WAVES_N, MIN_WAVES, VA_, VB_, CK_>(A, B, out, M, N, K, r, slab, stream)
+  if (va && vb) {
+    if (exact) LGEMM_CASE(4, 4, false); else LGEMM_CASE(4, 4, true);
+  } else if (va) {
+    LGEMM_CASE(4, 1, true);
+  } else if (vb) {
+    LGEMM_CASE(1, 4, true);
+  } else {
+    LGEMM_CASE(1, 1, true);
+  }
+#undef LGEMM_CASE
+}
+
+int launch(const float *A, const float *B, float *C, int M, int N, int K, const Resolved &r,
+           void *workspace, hipStream_t stream) {
+  float *out = r.splits > 1 ? static_cast<float *>(workspace) : C;
+  const long long slab = r.splits > 1 ? (long long)M * N : 0;
+  switch (r.k->id) {
+    case GEMM_KERNEL_MFMA_256x256:
+      launch_mfma<256, 256, 2, 2, 1>(A, B, out, M, N, K, r, slab, stream);
+      break;
+    case GEMM_KERNEL_MFMA_256x128:
+      launch_mfma<256, 128, 2, 2, 1>(A, B, out, M, N, K, r, slab, stream);
+      break;
+    case GEMM_KERNEL_MFMA_128x128:
+      launch_mfma<128, 128, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
+      break;
+    case GEMM_KERNEL_MFMA_64x64:
+      launch_mfma<64, 64, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
+      break;
+    case GEMM_KERNEL_VALU_64x64: {
+      const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
+      const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
+      if (exact)
+        hipLaunchKernelGGL(gemm::valu_gemm_kernel<false>, grid, dim3(gemm::kThreads), 0, stream, A,
+                           B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
+      else
+        hipLaunchKernelGGL(gemm::valu_gemm_kernel<true>, grid, dim3(gemm::kThreads), 0, stream, A,
+                           B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
+      break;
+    }
+    default:
+      return GEMM_ERR_INVALID_PLAN;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e);
+  if (r.splits > 1) {
+    const long long count = (long long)M * N;
+    const bool v4 = (count % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(workspace) % 16 == 0);
+    const long long items = v4 ? count / 4 : count;
+    const unsigned blocks =
+        static_cast<unsigned>(std::min<long long>(ceil_div(items, gemm::kThreads), 4 * kNumCus));
+    if (v4)
+      hipLaunchKernelGGL(gemm::splitk_reduce_kernel<4>, dim3(blocks), dim3(gemm::kThreads), 0,
+                         stream, static_cast<const float *>(workspace), C, count, r.splits);
+    else
+      hipLaunchKernelGGL(gemm::splitk_reduce_kernel<1>, dim3(blocks), dim3(gemm::kThreads), 0,
+                         stream, static_cast<const float *>(workspace), C, count, r.splits);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return GEMM_OK;
+}
+
+int launch_fill_zero(float *C, long long count, hipStream_t stream) {
+  const unsigned blocks =
+      static_cast<unsigned>(std::min<long long>(ceil_div(count, gemm::kThreads), 4 * kNumCus));
+  hipLaunchKernelGGL(gemm::fill_zero_kernel, dim3(blocks), dim3(gemm::kThreads), 0, stream, C,
+                     count);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? GEMM_OK : hip_fail(e);
+}
+
+// Common path for every entry point. `plan_in` null = planner. `own_ws`:
+// use (and grow) the library's per-device workspace instead of the caller's.
+int run(const float *A, const float *B, float *C, int M, int N, int K, const gemm_plan_t *plan_in,
+        void *workspace, size_t workspace_bytes, bool own_ws, hipStream_t stream) {
+  int st = validate(A, B, C, M, N, K);
+  if (st != GEMM_OK) return st;
+  int kernel = GEMM_KERNEL_AUTO, split = 1;
+  if (plan_in) {
+    kernel = plan_in->kernel;
+    split = plan_in->split_k;
+    if (kernel != GEMM_KERNEL_AUTO && (!find_kernel(kernel) || split < 1))
+      return GEMM_ERR_INVALID_PLAN;
+  }
+  if (kernel == GEMM_KERNEL_AUTO) plan(M, N, K, &kernel, &split);
+  Resolved r;
+  if (!resolve(M, N, K, kernel, split, &r)) return GEMM_ERR_INVALID_PLAN;
+  const size_t need = workspace_for(M, N, r);
+  if (!own_ws && need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return GEMM_ERR_WORKSPACE;
+  if (M == 0 || N == 0) return GEMM_OK;
+
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != GEMM_OK) return st;
+  if (K == 0) return launch_fill_zero(C, (long long)M * N, stream);
+
+  if (own_ws && need > 0) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_ws_bytes[dev] < need) {
+      if (g_ws[dev]) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e);
+        (void)hipFree(g_ws[dev]);
+        g_ws[dev] = nullptr;
+        g_ws_bytes[dev] = 0;
+      }
+      void *p = nullptr;
+      if (hipMalloc(&p, need) == hipSuccess) {
+        g_ws[dev] = p;
+        g_ws_bytes[dev] = need;
+      } else {
+        (void)hipGetLastError();
+      }
+    }
+    if (g_ws_bytes[dev] >= need) {
+      workspace = g_ws[dev];
+    } else {
+      // No workspace available: same kernel without the split.
+      if (!resolve(M, N, K, kernel, 1, &r)) return GEMM_ERR_INVALID_PLAN;
+      workspace = nullptr;
+    }
+  }
+  return launch(A, B, C, M, N, K, r, workspace, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K, hipStream_t stream) {
+  return run(A, B, C, M, N, K, nullptr, nullptr, 0, true, stream);
+}
+
+size_t gemm_f32_workspace_bytes(int M, int N, int K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  int kernel, split;
+  plan(M, N, K, &kernel, &split);
+  Resolved r;
+  if (!resolve(M, N, K, kernel, split, &r)) return 0;
+  return workspace_for(M, N, r);
+}
+
+int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K, void *workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  return run(A, B, C, M, N, K, nullptr, workspace, workspace_bytes, false, stream);
+}
+
+int gemm_f32_plan(int M, int N, int K, gemm_plan_t *out) {
+  if (!out) return GEMM_ERR_NULL_PTR;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_DIM;
+  int kernel, split;
+  plan(M, N, K, &kernel, &split);
+  Resolved r;
+  if (!resolve(M, N, K, kernel, split, &r)) return GEMM_ERR_INVALID_PLAN;
+  out->kernel = kernel;
+  out->split_k = r.splits;
+  out->k_chunk = r.k_chunk;
+  out->reserved = 0;
+  return GEMM_OK;
+}
+
+size_t gemm_f32_plan_workspace_bytes(int M, int N, int K, const gemm_plan_t *p) {
+  if (!p || M < 0 || N < 0 || K < 0) return 0;
+  int kernel = p->kernel, split = p->split_k;
+  if (kernel == GEMM_KERNEL_AUTO) plan(M, N, K, &kernel, &split);
+  Resolved r;
+  if (!resolve(M, N, K, kernel, split, &r)) return 0;
+  return workspace_for(M, N, r);
+}
+
+int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, int K,
+                       const gemm_plan_t *p, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (!p) return GEMM_ERR_INVALID_PLAN;
+  return run(A, B, C, M, N, K, p, workspace, workspace_bytes, false, stream);
+}
+
+const char *gemm_kernel_name(int kernel) {
+  if (kernel == GEMM_KERNEL_AUTO) return "auto";
+  const KernelInfo *k = find_kernel(kernel);
+  return k ? k->name : "unknown";
+}
+
+const char *gemm_status_string(int status) {
+  switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_INVALID_DIM: return "invalid dimension (negative or too large)";
+    case GEMM_ERR_NULL_PTR: return "null pointer with nonzero extent";
+    case GEMM_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_ERR_WORKSPACE: return "workspace missing or too small";
+    case GEMM_ERR_INVALID_PLAN: return "invalid plan (unknown kernel or split < 1)";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int gemm_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+/*
+ * libgemm: row-major FP32 matrix product C = A x B on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (yekq.top LeetGPU "matrix multiplication" walkthrough, the
+ * problem-statement and input/output sections; hpc.payai.win lesson 10
+ * "shared-memory tiled GEMM", section 1):
+ *
+ *   A is M x K, B is K x N, C is M x N, all dense, row-major FP32 in device
+ *   memory (element (r, c) of an R x S matrix sits at r*S + c, so the leading
+ *   dimensions are K, N and N). Every output is the length-K dot product
+ *   C[row][col] = sum_k A[row][k] * B[k][col].
+ *
+ * C is overwritten (alpha = 1, beta = 0); its prior contents are never read.
+ * K = 0 stores +0.0 into all of C (the empty sum). M = 0 or N = 0 does
+ * nothing. The sum is evaluated in FP32 (FP32 MFMA products and accumulation;
+ * with split-K, S partial sums over contiguous K ranges are added in
+ * ascending range order), so results are reproducible run to run for a given
+ * plan but are not in general bit-identical to a sequential sum.
+ *
+ * Calling convention shared by every entry point:
+ *   - Pointers are device pointers on the current HIP device; `stream` is a
+ *     HIP stream of that device (0 = the null stream). The work is enqueued
+ *     on `stream` and the call returns without synchronising: C is valid once
+ *     the stream reaches the end of the enqueued work.
+ *   - The caller owns A, B, C and any workspace, and keeps them alive and
+ *     unmodified until the stream has passed the work.
+ *   - A, B and C are `restrict`: C's bytes must not overlap A's or B's
+ *     (A and B may overlap each other). Pointers the call does not access
+ *     (all three when M or N is 0, A and B when K is 0) may be null.
+ *   - Errors are reported only through the returned status; nothing is
+ *     printed and nothing is thrown. Argument checks run before any HIP call,
+ *     so a rejected call has enqueued nothing.
+ *   - Thread-safe. The library-owned split-K workspace of gemm_f32 is one
+ *     buffer per device: gemm_f32 calls on one device that overlap in time on
+ *     different streams and both use split-K must be ordered by the caller
+ *     (or use gemm_f32_ex with their own workspaces).
+ */
+#ifndef LIBGEMM_GEMM_H
+#define LIBGEMM_GEMM_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_DIM = 1,      /* M, N or K negative, or a size too large to index */
+  GEMM_ERR_NULL_PTR = 2,         /* null A, B or C that the call would access
+                                    (A, B when M, N, K > 0; C when M, N > 0) */
+  GEMM_ERR_ALIAS = 3,            /* C overlaps A or B */
+  GEMM_ERR_WORKSPACE = 4,        /* workspace missing or smaller than required */
+  GEMM_ERR_INVALID_PLAN = 5,     /* unknown kernel id or split count < 1 */
+  GEMM_ERR_HIP = 6,              /* a HIP call failed; see gemm_last_hip_error() */
+  GEMM_ERR_UNSUPPORTED_DEVICE = 7 /* the current device is not gfx950 */
+};
+
+/* Kernel identifiers for explicit plans. Tile = the BM x BN output block one
+ * 256-thread workgroup computes. */
+enum {
+  GEMM_KERNEL_AUTO = 0,          /* let the planner choose */
+  GEMM_KERNEL_MFMA_256x256 = 1,  /* FP32 MFMA 32x32x2, 4 waves of 128x128 */
+  GEMM_KERNEL_MFMA_256x128 = 2,  /* FP32 MFMA 32x32x2, 4 waves of 128x64 */
+  GEMM_KERNEL_MFMA_128x128 = 3,  /* FP32 MFMA 32x32x2, 4 waves of 64x64 */
+  GEMM_KERNEL_MFMA_64x64 = 4,    /* FP32 MFMA 32x32x2, 4 waves of 32x32 */
+  GEMM_KERNEL_VALU_64x64 = 10    /* vector-FMA kernel, 4x4 register tile per lane */
+};
+
+/* An execution plan: which kernel, and how many contiguous K ranges
+ * ("split-K") the contraction is cut into. k_chunk is the length of each
+ * range (a multiple of the kernel's K step); split_k = ceil(K / k_chunk). */
+typedef struct gemm_plan {
+  int kernel;
+  int split_k;
+  int k_chunk;
+  int reserved;
+} gemm_plan_t;
+
+/* C = A x B with the planner's choice of kernel and split. When that plan
+ * splits K, the partial sums go to a library-owned per-device workspace that
+ * is allocated (hipMalloc) on first need and grown when a larger one is
+ * needed; if that allocation fails the call falls back to an unsplit plan.
+ * Returns a status code. */
+int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K,
+             hipStream_t stream);
+
+/* Bytes of workspace the planner's plan for (M, N, K) needs:
+ * 4 * split_k * M * N when it splits K, else 0. Returns 0 for invalid dims. */
+size_t gemm_f32_workspace_bytes(int M, int N, int K);
+
+/* As gemm_f32, with a caller-owned device workspace of workspace_bytes bytes
+ * (at least gemm_f32_workspace_bytes(M, N, K); may be null when that is 0).
+ * The workspace must not be used by other work until this call's work has
+ * completed on `stream`. Returns GEMM_ERR_WORKSPACE if it is too small. */
+int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K,
+                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The planner's plan for (M, N, K), written to *plan. Returns a status code. */
+int gemm_f32_plan(int M, int N, int K, gemm_plan_t *plan);
+
+/* Workspace bytes an explicit plan needs (0 for an invalid plan or dims). Only
+ * plan->kernel and plan->split_k are read. */
+size_t gemm_f32_plan_workspace_bytes(int M, int N, int K, const gemm_plan_t *plan);
+
+/* C = A x B with an explicit plan (plan->kernel, plan->split_k; split_k is
+ * clamped to the number of K steps). kernel = GEMM_KERNEL_AUTO means the
+ * planner's choice. workspace as for gemm_f32_ex. Returns a status code. */
+int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, int K,
+                       const gemm_plan_t *plan, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Static, human-readable name of a kernel id ("unknown" otherwise). */
+const char *gemm_kernel_name(int kernel);
+
+/* Static, human-readable text of a status code. */
+const char *gemm_status_string(int status);
+
+/* The hipError_t of the last failed HIP call made by this library on the
+ * calling thread (0 if none). */
+int gemm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_GEMM_H */

@@ -1,0 +1,236 @@
+"""GPU parity of libgemm against the CPU oracle, through the C ABI.
+
+Floating-point inputs: every element within |C - ref| <= 1e-5 * S + 1e-6,
+S = sum_k |A_ik B_kj| (the oracle's second output). Integer inputs whose every
+partial sum is exact in FP32: raw bits equal. C starts as NaN before every
+call, so an output that is never written fails.
+"""
+import numpy as np
+import pytest
+
+import gemm_inputs
+import oracle
+from fp32_gemm_07_amd import binding
+from gpu_util import nan_buffer, run, say, to_dev, torch
+from parity import assert_bits_equal, assert_within_bound
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [w for w in gemm_inputs.WORKLOADS if w.M * w.N * w.K <= 1 << 30]
+LARGE = [w for w in gemm_inputs.WORKLOADS if w.M * w.N * w.K > 1 << 30]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build(force=False)
+    binding.load()
+    torch()
+
+
+# ---------------------------------------------------------------------------
+# Standing workloads, planner's choice (the launch configuration the bench times).
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_workload_full_parity(w):
+    say(f"workload {w.name} plan {binding.gemm_f32_plan(w.M, w.N, w.K)}")
+    A, B = gemm_inputs.draw_workload(w)
+    C = run(A, B)
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, w.name)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_workload_small_integers_bit_exact(w):
+    say(f"workload {w.name} (integers)")
+    A, B = gemm_inputs.draw_workload(w, integer=True)
+    C = run(A, B)
+    C_ref = oracle.gemm_i64(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    assert_bits_equal(C, C_ref, w.name + " int")
+
+
+@pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
+def test_workload_full_size_sampled(w):
+    """Full size, planner's plan: sampled outputs against the oracle one by one,
+    every output finite, and a rerun bit-identical (fixed split-K order)."""
+    t = torch()
+    say(f"workload {w.name} plan {binding.gemm_f32_plan(w.M, w.N, w.K)}")
+    A, B = gemm_inputs.draw_workload(w)
+    dA, dB = to_dev(A), to_dev(B)
+    dC = nan_buffer(w.M * w.N)
+    s = t.cuda.current_stream()
+    binding.gemm_f32(dA, dB, dC, w.M, w.N, w.K, s.cuda_stream)
+    s.synchronize()
+    C = dC.cpu().numpy().reshape(w.M, w.N)
+    assert np.isfinite(C).all()
+    rows, cols = gemm_inputs.sample_indices(w.M, w.N, 3000, seed=w.seed)
+    ref, S = oracle.gemm_entries(A, B, rows, cols)
+    assert_within_bound(C[rows, cols], ref, S, w.name)
+    dC2 = nan_buffer(w.M * w.N)
+    binding.gemm_f32(dA, dB, dC2, w.M, w.N, w.K, s.cuda_stream)
+    s.synchronize()
+    assert t.equal(dC.view(t.int32), dC2.view(t.int32))
+
+
+@pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
+def test_workload_full_size_integers_sampled(w):
+    say(f"workload {w.name} (integers, sampled)")
+    A, B = gemm_inputs.draw_workload(w, integer=True)
+    C = run(A, B)
+    rows, cols = gemm_inputs.sample_indices(w.M, w.N, 3000, seed=w.seed + 100)
+    ref, _ = oracle.gemm_entries(A, B, rows, cols)
+    assert_bits_equal(C[rows, cols], ref, w.name + " int")
+    assert np.all(C == np.round(C)) and np.abs(C).max() <= 2 ** 24
+
+
+# ---------------------------------------------------------------------------
+# Every kernel, ragged shapes spanning several tiles, with and without split-K.
+
+KERNELS = list(binding.KERNELS.items())
+RAGGED = [(1, 1, 1), (32, 2, 32), (33, 17, 31), (64, 16, 64), (65, 129, 63), (127, 40, 129),
+          (257, 33, 255), (300, 513, 260), (128, 96, 112), (512, 64, 513)]
+
+
+@pytest.mark.parametrize("kname,kid", KERNELS, ids=[k for k, _ in KERNELS])
+@pytest.mark.parametrize("M,K,N", RAGGED, ids=[f"{m}x{k}x{n}" for m, k, n in RAGGED])
+@pytest.mark.parametrize("split", [1, 3])
+def test_kernel_ragged_parity(kname, kid, M, K, N, split):
+    say(f"kernel {kname} {M}x{K}x{N} split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=M * 7 + K * 3 + N)
+    C = run(A, B, plan=binding.make_plan(kid, split))
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, f"{kname} {M}x{K}x{N}/{split}")
+
+
+@pytest.mark.parametrize("kname,kid", KERNELS, ids=[k for k, _ in KERNELS])
+@pytest.mark.parametrize("M,K,N", [(32, 2, 32), (65, 129, 63), (300, 513, 260), (256, 64, 256)])
+@pytest.mark.parametrize("split", [1, 4])
+def test_kernel_integers_bit_exact(kname, kid, M, K, N, split):
+    """Integer inputs pin the MFMA operand and accumulator lane layouts: a
+    32x2 by 2x32 product is exactly one v_mfma_f32_32x32x2_f32."""
+    say(f"kernel {kname} int {M}x{K}x{N} split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "int", seed=K)
+    C = run(A, B, plan=binding.make_plan(kid, split))
+    C_ref = oracle.gemm_i64(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    assert_bits_equal(C, C_ref, f"{kname} int {M}x{K}x{N}/{split}")
+
+
+# ---------------------------------------------------------------------------
+# Memory safety, degenerate sizes, API contract.
+
+@pytest.mark.parametrize("kname,kid", KERNELS, ids=[k for k, _ in KERNELS])
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_guard_bands_untouched(kname, kid, misalign):
+    """A, B and C sit inside one NaN-filled buffer with NaN guards around each;
+    a read past an operand would turn outputs into NaN, a write past C would
+    change a guard. misalign = 1 shifts every operand by one float (the 4-byte
+    load path)."""
+    t = torch()
+    M, K, N, split = 97, 53, 71, 2
+    say(f"guard bands {kname} misalign {misalign}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=21)
+    g = 256 + misalign
+    offA = g
+    offB = offA + M * K + g
+    offC = offB + K * N + g
+    total = offC + M * N + g
+    buf = nan_buffer(total)
+    buf[offA:offA + M * K] = to_dev(A.ravel())
+    buf[offB:offB + K * N] = to_dev(B.ravel())
+    plan = binding.make_plan(kid, split)
+    need = binding.gemm_f32_plan_workspace_bytes(M, N, K, plan)
+    ws = t.empty((max(need // 4, 1),), dtype=t.float32, device="cuda:0")
+    base = buf.data_ptr()
+    s = t.cuda.current_stream()
+    binding.gemm_f32_with_plan(base + 4 * offA, base + 4 * offB, base + 4 * offC, M, N, K, plan,
+                               ws, need, s.cuda_stream)
+    s.synchronize()
+    host = buf.cpu().numpy()
+    C = host[offC:offC + M * N].reshape(M, N)
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, "guarded C")
+    guards = np.concatenate([host[:offA], host[offA + M * K:offB], host[offB + K * N:offC],
+                             host[offC + M * N:]])
+    assert np.isnan(guards).all()
+    np.testing.assert_array_equal(host[offA:offA + M * K], A.ravel())
+    np.testing.assert_array_equal(host[offB:offB + K * N], B.ravel())
+
+
+def test_k_zero_writes_positive_zeros():
+    t = torch()
+    say("K = 0")
+    dC = nan_buffer(5 * 7)
+    binding.gemm_f32(0, 0, dC, 5, 7, 0, t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    assert (dC.view(t.int32) == 0).all()
+
+
+def test_empty_outputs_leave_memory_untouched():
+    t = torch()
+    say("M = 0 / N = 0")
+    dC = nan_buffer(16)
+    dA = to_dev(np.ones((4, 4), np.float32))
+    binding.gemm_f32(dA, dA, dC, 0, 4, 4, 0)
+    binding.gemm_f32(dA, dA, dC, 4, 0, 4, 0)
+    t.cuda.synchronize()
+    assert t.isnan(dC).all()
+
+
+def test_alias_rejected_before_any_work():
+    t = torch()
+    say("alias")
+    dA = to_dev(np.ones((8, 8), np.float32))
+    with pytest.raises(binding.GemmError) as e:
+        binding.gemm_f32(dA, dA, dA.data_ptr() + 16, 8, 8, 8, 0)
+    assert e.value.status == binding.GEMM_ERR_ALIAS
+    t.cuda.synchronize()
+    assert (dA == 1).all()
+
+
+def test_transpose_identity():
+    """(AB)^T = B^T A^T: the product of the transposed operands is the
+    transpose of the product, within the bound, on the GPU."""
+    say("transpose identity")
+    A, B = gemm_inputs.draw(300, 129, 170, "uniform", seed=8)
+    C = run(A, B)
+    Ct = run(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T))
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, "C")
+    assert_within_bound(Ct.T, C_ref, S, "C from transposes")
+
+
+def test_non_default_stream():
+    t = torch()
+    say("non-default stream")
+    A, B = gemm_inputs.draw(256, 512, 256, "uniform", seed=4)
+    stream = t.cuda.Stream()
+    C = run(A, B, stream=stream)
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, "side stream")
+
+
+def test_caller_workspace_matches_library_workspace():
+    say("gemm_f32_ex vs gemm_f32 (split-K)")
+    M, K, N = 256, 16384, 256
+    plan = binding.gemm_f32_plan(M, N, K)
+    assert plan.split_k > 1
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=6)
+    C1 = run(A, B)
+    C2 = run(A, B, entry="gemm_f32_ex")
+    assert_bits_equal(C1, C2, "ex vs library workspace")
+    rows, cols = gemm_inputs.sample_indices(M, N, 500)
+    ref, S = oracle.gemm_entries(A, B, rows, cols)
+    assert_within_bound(C1[rows, cols], ref, S, "split-K")
+
+
+def test_splitk_deterministic_and_matches_unsplit_on_integers():
+    say("split-K determinism")
+    M, K, N = 300, 4000, 200
+    A, B = gemm_inputs.draw(M, K, N, "int", seed=9)
+    C_ref = oracle.gemm_i64(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    for split in (1, 2, 7, 16):
+        plan = binding.make_plan(binding.GEMM_KERNEL_MFMA_128x128, split)
+        C = run(A, B, plan=plan)
+        assert_bits_equal(C, C_ref, f"split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=9)
+    plan = binding.make_plan(binding.GEMM_KERNEL_MFMA_128x128, 7)
+    assert_bits_equal(run(A, B, plan=plan), run(A, B, plan=plan), "rerun")
