@@ -68,6 +68,24 @@ class gemm_plan_t(ctypes.Structure):
 _lib = None
 
 
+def _share_hip_runtime() -> None:
+    """Make libgemm use the HIP runtime the caller's memory and streams come from.
+
+    PyTorch-ROCm wheels bundle their own libamdhip64 (and HSA runtime) under
+    the soname libamdhip64.so.7. A process that ends up with two HIP runtimes
+    cannot use the GPU from the second one (device enumeration fails), and
+    pointers and streams of one are meaningless to the other. libgemm names
+    its runtime only by soname, and the dynamic linker resolves a soname to a
+    library already loaded under it, so loading torch first makes libgemm
+    bind to torch's runtime. Without torch installed, the system ROCm runtime
+    is used.
+    """
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def library_path() -> str:
     return LIB_PATH
 
@@ -79,6 +97,7 @@ def load():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libgemm is not built ({LIB_PATH} missing); run "
                                "fp32_gemm_07_amd.build.build() first")
+        _share_hip_runtime()
         lib = ctypes.CDLL(LIB_PATH)
         vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         plan_p = ctypes.POINTER(gemm_plan_t)
