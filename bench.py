@@ -47,7 +47,27 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle's CPU-baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel", default="auto", choices=["auto", *binding.KERNELS],
+                   help="time this kernel instead of the planner's choice")
+    p.add_argument("--split", type=int, default=1, help="split-K ranges for --kernel")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="instead of the bench, run a plain device-to-device copy of this many MiB "
+                        "--steps times (calibrates the HBM byte counters against a known size)")
     return p.parse_args(argv)
+
+
+def copy_probe(mib: int, steps: int) -> int:
+    """A plain copy of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+                      "launches": steps, "ok": bool(torch.equal(dst, src))}), flush=True)
+    return 0
 
 
 def cpu_baseline(A, B, C_gpu, target_s: float):
@@ -95,23 +115,28 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_probe_mib:
+        return copy_probe(args.copy_probe_mib, args.steps)
     w = gemm_inputs.BY_NAME[args.workload]
     M, N, K = w.M, w.N, w.K
-    plan = binding.gemm_f32_plan(M, N, K)
+    if args.kernel == "auto":
+        plan = binding.gemm_f32_plan(M, N, K)
+    else:
+        plan = binding.make_plan(binding.KERNELS[args.kernel], args.split)
     kname = binding.gemm_kernel_name(plan.kernel)
+    ws_bytes = binding.gemm_f32_plan_workspace_bytes(M, N, K, plan)
 
     A, B = gemm_inputs.draw_workload(w)
     dev = torch.device("cuda:0")
     dA = torch.from_numpy(A).to(dev)
     dB = torch.from_numpy(B).to(dev)
     dC = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
-    ws_bytes = binding.gemm_f32_workspace_bytes(M, N, K)
     ws = torch.empty((max(ws_bytes // 4, 1),), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     h = stream.cuda_stream
 
     def step():
-        binding.gemm_f32_ex(dA, dB, dC, M, N, K, ws, ws_bytes, h)
+        binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, ws, ws_bytes, h)
 
     for _ in range(args.warmup):
         step()
@@ -151,7 +176,7 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": w.name, "M": M, "N": N, "K": K, "dist": w.dist, "seed": w.seed,
-            "plan": {"kernel": kname, "split_k": plan.split_k, "k_chunk": plan.k_chunk},
+            "plan": {"kernel": kname, "split_k": plan.split_k if args.kernel == "auto" else args.split},
             "parallelism": "1 GPU",
         },
         "pct_of_fp32_peak": round(100 * value / peak, 2),

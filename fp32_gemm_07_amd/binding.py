@@ -29,13 +29,31 @@ GEMM_KERNEL_MFMA_256x256 = 1
 GEMM_KERNEL_MFMA_256x128 = 2
 GEMM_KERNEL_MFMA_128x128 = 3
 GEMM_KERNEL_MFMA_64x64 = 4
+GEMM_KERNEL_MFMA_256x256_W8 = 5
 GEMM_KERNEL_VALU_64x64 = 10
+GEMM_KERNEL_MFMA16_256x256 = 11
+GEMM_KERNEL_MFMA16_256x256_W8 = 12
+GEMM_KERNEL_MFMA16_256x128 = 13
+GEMM_KERNEL_MFMA16_128x128 = 14
+GEMM_KERNEL_MFMA16_64x64 = 15
+GEMM_KERNEL_MFMA16_256x256_K16 = 16
+GEMM_KERNEL_MFMA16_128x128_K16 = 17
+GEMM_KERNEL_MFMA16_256x128_K16 = 18
 
 KERNELS = {
-    "mfma_256x256": GEMM_KERNEL_MFMA_256x256,
-    "mfma_256x128": GEMM_KERNEL_MFMA_256x128,
-    "mfma_128x128": GEMM_KERNEL_MFMA_128x128,
-    "mfma_64x64": GEMM_KERNEL_MFMA_64x64,
+    "mfma32_256x256": GEMM_KERNEL_MFMA_256x256,
+    "mfma32_256x256_w8": GEMM_KERNEL_MFMA_256x256_W8,
+    "mfma32_256x128": GEMM_KERNEL_MFMA_256x128,
+    "mfma32_128x128": GEMM_KERNEL_MFMA_128x128,
+    "mfma32_64x64": GEMM_KERNEL_MFMA_64x64,
+    "mfma16_256x256": GEMM_KERNEL_MFMA16_256x256,
+    "mfma16_256x256_w8": GEMM_KERNEL_MFMA16_256x256_W8,
+    "mfma16_256x128": GEMM_KERNEL_MFMA16_256x128,
+    "mfma16_128x128": GEMM_KERNEL_MFMA16_128x128,
+    "mfma16_64x64": GEMM_KERNEL_MFMA16_64x64,
+    "mfma16_256x256_k16": GEMM_KERNEL_MFMA16_256x256_K16,
+    "mfma16_128x128_k16": GEMM_KERNEL_MFMA16_128x128_K16,
+    "mfma16_256x128_k16": GEMM_KERNEL_MFMA16_256x128_K16,
     "valu_64x64": GEMM_KERNEL_VALU_64x64,
 }
 

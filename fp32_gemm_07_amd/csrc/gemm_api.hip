@@ -32,10 +32,19 @@ struct KernelInfo {
 };
 
 constexpr KernelInfo kKernels[] = {
-    {GEMM_KERNEL_MFMA_256x256, 256, 256, 16, "mfma_f32_256x256x16"},
-    {GEMM_KERNEL_MFMA_256x128, 256, 128, 16, "mfma_f32_256x128x16"},
-    {GEMM_KERNEL_MFMA_128x128, 128, 128, 16, "mfma_f32_128x128x16"},
-    {GEMM_KERNEL_MFMA_64x64, 64, 64, 16, "mfma_f32_64x64x16"},
+    {GEMM_KERNEL_MFMA_256x256, 256, 256, 16, "mfma32_f32_256x256x16"},
+    {GEMM_KERNEL_MFMA_256x256_W8, 256, 256, 16, "mfma32_f32_256x256x16_w8"},
+    {GEMM_KERNEL_MFMA_256x128, 256, 128, 16, "mfma32_f32_256x128x16"},
+    {GEMM_KERNEL_MFMA_128x128, 128, 128, 16, "mfma32_f32_128x128x16"},
+    {GEMM_KERNEL_MFMA_64x64, 64, 64, 16, "mfma32_f32_64x64x16"},
+    {GEMM_KERNEL_MFMA16_256x256, 256, 256, 32, "mfma16_f32_256x256x32"},
+    {GEMM_KERNEL_MFMA16_256x256_W8, 256, 256, 32, "mfma16_f32_256x256x32_w8"},
+    {GEMM_KERNEL_MFMA16_256x128, 256, 128, 32, "mfma16_f32_256x128x32"},
+    {GEMM_KERNEL_MFMA16_128x128, 128, 128, 32, "mfma16_f32_128x128x32"},
+    {GEMM_KERNEL_MFMA16_64x64, 64, 64, 32, "mfma16_f32_64x64x32"},
+    {GEMM_KERNEL_MFMA16_256x256_K16, 256, 256, 16, "mfma16_f32_256x256x16"},
+    {GEMM_KERNEL_MFMA16_128x128_K16, 128, 128, 16, "mfma16_f32_128x128x16"},
+    {GEMM_KERNEL_MFMA16_256x128_K16, 256, 128, 16, "mfma16_f32_256x128x16"},
     {GEMM_KERNEL_VALU_64x64, 64, 64, 16, "valu_f32_64x64x16"},
 };
 
@@ -74,22 +83,22 @@ size_t workspace_for(int M, int N, const Resolved &r) {
   return r.splits > 1 ? sizeof(float) * (size_t)r.splits * (size_t)M * (size_t)N : 0;
 }
 
-// The planner. Rules of thumb for one MI355X (256 CUs):
-//  - enough 256x256 tiles to give every CU one (>= 192): 256x256, no split;
-//  - few output tiles but a long K: 256x256 (or 128x128 for narrow outputs)
-//    split along K until about 256 workgroups, keeping each K range >= 1024;
-//  - otherwise the smallest MFMA tile that still gives about one workgroup
-//    per CU.
+// The planner. Rules of thumb for one MI355X (256 CUs), from measured sweeps:
+//  - enough 256x256 tiles to give every CU one (>= 192): the 8-wave 256x256
+//    32x32x2 kernel, no split (134 TFLOP/s at 4096^3);
+//  - few output tiles but a long K: split K until about 256 workgroups,
+//    keeping each K range >= 1024 (256x256 tiles for wide outputs, 128x128
+//    for narrow ones);
+//  - otherwise 64x64 tiles of the 16x16x4 kernel (one workgroup per CU at
+//    1024x1024 outputs).
 void plan(int M, int N, int K, int *kernel, int *split) {
   *split = 1;
   const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t128 = ceil_div(M, 128) * ceil_div(N, 128);
-  const long long t64 = ceil_div(M, 64) * ceil_div(N, 64);
   if (t256 >= 192) {
-    *kernel = GEMM_KERNEL_MFMA_256x256;
+    *kernel = GEMM_KERNEL_MFMA_256x256_W8;
     return;
   }
-  // Long-K shapes: split K.
   const long long kmin = 1024;
   if (K >= 4 * kmin) {
     const bool wide = M >= 256 && N >= 256;
@@ -97,7 +106,7 @@ void plan(int M, int N, int K, int *kernel, int *split) {
     long long s = std::max<long long>(1, kNumCus / std::max<long long>(1, tiles));
     s = std::min<long long>(s, K / kmin);
     if (s > 1 || tiles >= 96) {
-      *kernel = wide ? GEMM_KERNEL_MFMA_256x256 : GEMM_KERNEL_MFMA_128x128;
+      *kernel = wide ? GEMM_KERNEL_MFMA_256x256_W8 : GEMM_KERNEL_MFMA_128x128;
       *split = static_cast<int>(s);
       return;
     }
@@ -106,8 +115,7 @@ void plan(int M, int N, int K, int *kernel, int *split) {
     *kernel = GEMM_KERNEL_MFMA_128x128;
     return;
   }
-  (void)t64;
-  *kernel = GEMM_KERNEL_MFMA_64x64;
+  *kernel = GEMM_KERNEL_MFMA16_64x64;
 }
 
 // ---------------------------------------------------------------------------
@@ -162,52 +170,92 @@ int validate(const float *A, const float *B, const float *C, int M, int N, int K
 
 // ---------------------------------------------------------------------------
 // Launch helpers.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES, int VA, int VB, bool CHECK>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WPE, int VA, int VB,
+          bool CHECK>
 void launch_mfma_t(const float *A, const float *B, float *out, int M, int N, int K,
                    const Resolved &r, long long slab, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
-  hipLaunchKernelGGL((gemm::mfma_gemm_kernel<BM, BN, 16, WAVES_M, WAVES_N, VA, VB, CHECK, MIN_WAVES>),
-                     grid, dim3(gemm::kThreads), 0, stream, A, B, out, M, N, K, r.k_chunk,
-                     static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits, slab);
+  hipLaunchKernelGGL(
+      (gemm::mfma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, VA, VB, CHECK, WPE>), grid,
+      dim3(64 * WAVES_M * WAVES_N), 0, stream, A, B, out, M, N, K, r.k_chunk,
+      static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits, slab);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MIN_WAVES>
-void launch_mfma(const float *A, const float *B, float *out, int M, int N, int K,
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// Picks the load width and edge-check variant of one tile configuration.
+// WPE = waves per SIMD the register allocation is sized for. Configurations
+// with SCALAR = false have no 4-byte-load variants (they would not fit their
+// register budget): they return false for shapes that need them.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WPE, bool SCALAR>
+bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K,
                  const Resolved &r, long long slab, hipStream_t stream) {
-  const bool va = (K % 4 == 0) && (reinterpret_cast<uintptr_t>(A) % 16 == 0);
-  const bool vb = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(B) % 16 == 0);
-  const bool exact = (M % BM == 0) && (N % BN == 0) && (K % 16 == 0) && (r.k_chunk % 16 == 0);
-#define LGEMM_CASE(VA_, VB_, CK_) \
-  launch_mfma_t<BM, BN, WAVES_M, WAVES_N, MIN_WAVES, VA_, VB_, CK_>(A, B, out, M, N, K, r, slab, stream)
+  const bool va = (K % 4 == 0) && aligned16(A);
+  const bool vb = (N % 4 == 0) && aligned16(B);
+  const bool exact = (M % BM == 0) && (N % BN == 0) && (K % BK == 0) && (r.k_chunk % BK == 0);
+#define LGEMM_CASE(VA_, VB_, CK_)                                                             \
+  launch_mfma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, WPE, VA_, VB_, CK_>(A, B, out, M, N, K, r, \
+                                                                     slab, stream)
   if (va && vb) {
     if (exact) LGEMM_CASE(4, 4, false); else LGEMM_CASE(4, 4, true);
-  } else if (va) {
-    LGEMM_CASE(4, 1, true);
-  } else if (vb) {
-    LGEMM_CASE(1, 4, true);
-  } else {
-    LGEMM_CASE(1, 1, true);
+    return true;
+  }
+  if constexpr (SCALAR) {
+    if (va) LGEMM_CASE(4, 1, true);
+    else if (vb) LGEMM_CASE(1, 4, true);
+    else LGEMM_CASE(1, 1, true);
+    return true;
   }
 #undef LGEMM_CASE
+  return false;
 }
 
-int launch(const float *A, const float *B, float *C, int M, int N, int K, const Resolved &r,
-           void *workspace, hipStream_t stream) {
-  float *out = r.splits > 1 ? static_cast<float *>(workspace) : C;
-  const long long slab = r.splits > 1 ? (long long)M * N : 0;
+// Launch the kernel of r.k (falling back to a configuration with 4-byte
+// loads where the chosen one has none for this shape).
+void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N, int K,
+                        const Resolved &r, long long slab, hipStream_t stream) {
   switch (r.k->id) {
     case GEMM_KERNEL_MFMA_256x256:
-      launch_mfma<256, 256, 2, 2, 1>(A, B, out, M, N, K, r, slab, stream);
-      break;
+      launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA_256x256_W8:
+      if (!launch_mfma<32, 256, 256, 16, 2, 4, 2, false>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
     case GEMM_KERNEL_MFMA_256x128:
-      launch_mfma<256, 128, 2, 2, 1>(A, B, out, M, N, K, r, slab, stream);
-      break;
+      launch_mfma<32, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
     case GEMM_KERNEL_MFMA_128x128:
-      launch_mfma<128, 128, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
-      break;
+      launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
     case GEMM_KERNEL_MFMA_64x64:
-      launch_mfma<64, 64, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
-      break;
+      launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_256x256:
+      launch_mfma<16, 256, 256, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_256x256_W8:
+      if (!launch_mfma<16, 256, 256, 32, 2, 4, 2, false>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<16, 256, 256, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_256x128:
+      launch_mfma<16, 256, 128, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_128x128:
+      launch_mfma<16, 128, 128, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_64x64:
+      launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_256x256_K16:
+      launch_mfma<16, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_128x128_K16:
+      launch_mfma<16, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_256x128_K16:
+      launch_mfma<16, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
@@ -217,11 +265,16 @@ int launch(const float *A, const float *B, float *C, int M, int N, int K, const 
       else
         hipLaunchKernelGGL(gemm::valu_gemm_kernel<true>, grid, dim3(gemm::kThreads), 0, stream, A,
                            B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
-      break;
+      return;
     }
-    default:
-      return GEMM_ERR_INVALID_PLAN;
   }
+}
+
+int launch(const float *A, const float *B, float *C, int M, int N, int K, const Resolved &r,
+           void *workspace, hipStream_t stream) {
+  float *out = r.splits > 1 ? static_cast<float *>(workspace) : C;
+  const long long slab = r.splits > 1 ? (long long)M * N : 0;
+  launch_gemm_kernel(A, B, out, M, N, K, r, slab, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
   if (r.splits > 1) {

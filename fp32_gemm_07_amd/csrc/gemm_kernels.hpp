@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gemm {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -67,59 +69,106 @@ __device__ inline TileCoord map_tile(int bid, int tiles_m, int tiles_n, int spli
 // ---------------------------------------------------------------------------
 // FP32 MFMA kernel.
 //
-// BM x BN output tile per workgroup of 4 waves arranged WAVES_M x WAVES_N;
-// each wave owns a WM x WN sub-tile made of (WM/32) x (WN/32) accumulator
-// blocks of v_mfma_f32_32x32x2_f32.
+// BM x BN output tile per workgroup of 4 or 8 waves arranged WAVES_M x
+// WAVES_N; each wave owns a WM x WN sub-tile made of (WM/MI) x (WN/MI)
+// accumulator blocks of one FP32 matrix instruction:
+//   MI = 32: v_mfma_f32_32x32x2_f32 (32x2 by 2x32, 16 accumulators per lane);
+//   MI = 16: v_mfma_f32_16x16x4_f32 (16x4 by 4x16, 4 accumulators per lane).
+// Both retire 256 FLOP per clock per CU; on MI355X the chip holds a higher
+// clock under the 16x16 form, so the planner prefers it for large products.
 //
-// Operand layout of that instruction (CDNA3/CDNA4 ISA, matrix instructions):
-// lane l supplies A[i = l % 32][kk = l / 32] and B[kk = l / 32][j = l % 32]
-// for a 32x2 by 2x32 product; its 16 accumulator values are the outputs at
-// column j = l % 32 and rows 8*(v/4) + 4*(l/32) + v%4, v = 0..15.
+// Operand layout (CDNA3/CDNA4 ISA, matrix instructions): the 64 lanes form
+// NQ = 64/MI groups q = lane / MI of MI lanes each; lane (q, i) supplies
+// A[row i][kk = q] and B[kk = q][column i]. Accumulator v of lane (q, i)
+// holds output column i and row 8*(v/4) + 4*q + v%4 (MI = 32) or
+// 4*q + v (MI = 16).
 //
-// Which real k index an instruction's kk slot carries is free, as long as A
-// and B agree: within a K step of BK, instruction s (s = 0..BK/2-1) takes
-// k = s for lanes 0-31 and k = BK/2 + s for lanes 32-63. A lane therefore
-// reads BK/2 consecutive k of one A row (two 16-byte LDS reads) and one B
-// column at BK/2 consecutive k.
+// Which real k index a group's kk slot carries is free, as long as A and B
+// agree: within a K step of BK, instruction s (s = 0..KS-1, KS = BK/NQ) takes
+// k = q*KS + s for lane group q. A lane therefore reads KS consecutive k of
+// one A row (one 16-byte LDS read per 4 instructions) and one B column at KS
+// consecutive k.
 //
-// LDS layout per buffer: A row-major [BM][BK + 4] (the 4-float pad makes the
-// 16-byte row reads of 16 consecutive rows cover all 64 banks once), B
-// row-major [BK][BN + 4] (the pad puts the two half-waves, which read rows
-// BK/2 apart, on disjoint bank halves).
+// LDS layout per buffer: A row-major [BM][BK + 4], B row-major [BK][BN + 4];
+// the pads shift consecutive rows across banks.
 //
 // VA / VB: 4 = 16-byte global loads (needs K % 4 == 0, resp. N % 4 == 0 and
 // 16-byte aligned base pointers), 1 = 4-byte loads for any shape.
 // CHECK = false only when the tile grid covers M and N exactly and every K
 // range is a whole number of K steps; otherwise each load is predicated and
 // zero-filled and each store is predicated.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N>
 struct MfmaShape {
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int NQ = 64 / MI;    // lane groups = k per instruction
+  static constexpr int ACC = MI * MI / 64;  // accumulators per lane per block
   static constexpr int WM = BM / WAVES_M;
   static constexpr int WN = BN / WAVES_N;
-  static constexpr int FM = WM / 32;
-  static constexpr int FN = WN / 32;
-  static constexpr int KH = BK / 2;
+  static constexpr int FM = WM / MI;
+  static constexpr int FN = WN / MI;
+  static constexpr int KS = BK / NQ;    // instructions per K step
+  static constexpr int NG = KS / 4;     // fragment groups of 4 instructions per K step
   static constexpr int LDA = BK + 4;
   static constexpr int LDB = BN + 4;
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves per workgroup");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile is whole 32x32 blocks");
-  static_assert(BK % 8 == 0, "BK/2 k-steps, read in 16-byte groups");
+  static_assert(MI == 16 || MI == 32, "16x16x4 or 32x32x2 FP32 MFMA");
+  static_assert(NWAVES == 4 || NWAVES == 8, "4 or 8 waves per workgroup");
+  static_assert(WM % MI == 0 && WN % MI == 0, "wave tile is whole blocks");
+  static_assert(KS % 4 == 0 && (NG == 1 || NG % 2 == 0),
+                "K step is one or an even number of 4-instruction groups");
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int VA, int VB, bool CHECK,
-          int MIN_WAVES>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(MIN_WAVES, MIN_WAVES == 1 ? 1 : 8)))
+template <int MI>
+struct Mfma;
+template <>
+struct Mfma<32> {
+  typedef floatx16 acc_t;
+  static __device__ inline acc_t run(float a, float b, const acc_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  // output row of accumulator v for lane group q
+  static __device__ inline int row(int q, int v) { return 8 * (v >> 2) + 4 * q + (v & 3); }
+};
+template <>
+struct Mfma<16> {
+  typedef floatx4 acc_t;
+  static __device__ inline acc_t run(float a, float b, const acc_t &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ inline int row(int q, int v) { return 4 * q + v; }
+};
+
+// Software pipeline of one K step t (buffer cur = t % 2), NG groups g of 4
+// instructions, fragments double buffered in registers (slot = g % 2):
+//   group g < NG-1: MFMAs of instruction 4g, then LDS reads of group g+1's
+//                   fragments, then the MFMAs of instructions 4g+1..4g+3;
+//   group NG-1:     (all reads of buffer cur are issued) store the staged
+//                   global data of step t+1 into buffer cur^1, barrier, MFMAs
+//                   of instruction 4g, then read group 0 of step t+1 from
+//                   buffer cur^1 and issue the global loads of step t+2, then
+//                   the remaining MFMAs.
+// Each fragment read has at least 3 x FM x FN MFMAs to land, each global load
+// a whole K step, and the barrier and LDS stores sit where the matrix pipe
+// still has queued work. __builtin_amdgcn_sched_barrier(0) keeps the compiler
+// from regrouping the segments.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int VA, int VB, bool CHECK,
+          int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
+                                                      64 * WAVES_M * WAVES_N),
+                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
                       float *__restrict__ C, int M, int N, int K, int k_chunk,
                       int tiles_m, int tiles_n, int splits, long long slab) {
-  using S = MfmaShape<BM, BN, BK, WAVES_M, WAVES_N>;
-  constexpr int FM = S::FM, FN = S::FN, KH = S::KH, LDA = S::LDA, LDB = S::LDB;
+  using S = MfmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N>;
+  using Op = Mfma<MI>;
+  using acc_t = typename Op::acc_t;
+  constexpr int T = S::THREADS;
+  constexpr int FM = S::FM, FN = S::FN, KS = S::KS, NG = S::NG, LDA = S::LDA, LDB = S::LDB;
   constexpr int A_CPR = BK / VA;              // load chunks per A tile row
-  constexpr int A_PER_T = BM * A_CPR / kThreads;
+  constexpr int A_PER_T = BM * A_CPR / T;
   constexpr int B_CPR = BN / VB;              // load chunks per B tile row
-  constexpr int B_PER_T = BK * B_CPR / kThreads;
-  static_assert(BM * A_CPR % kThreads == 0 && BK * B_CPR % kThreads == 0, "even load split");
+  constexpr int B_PER_T = BK * B_CPR / T;
+  static_assert(BM * A_CPR % T == 0 && BK * B_CPR % T == 0, "even load split");
 
   __shared__ __attribute__((aligned(16))) float As[2][BM * LDA];
   __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
@@ -135,67 +184,50 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int half = lane >> 5;   // which k half of the K step this lane carries
-  const int l32 = lane & 31;
+  const int q = lane / MI;       // lane group: which k slot of each instruction
+  const int li = lane % MI;      // row of A / column of B within a block
 
-  // Per-thread global source pointers at the first K step, and LDS offsets.
-  const float *pa[A_PER_T];
-  int a_lds[A_PER_T];
-  bool a_row_ok[A_PER_T];
-  int a_k[A_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int e = tid + kThreads * i;
-    const int r = e / A_CPR, c = e % A_CPR;
-    const int row = m0 + r;
-    a_row_ok[i] = !CHECK || row < M;
-    const int row_c = (CHECK && row >= M) ? (M - 1) : row;
-    a_k[i] = k_begin + c * VA;
-    pa[i] = A + (long long)row_c * K + a_k[i];
-    a_lds[i] = r * LDA + c * VA;
-  }
-  const float *pb[B_PER_T];
-  int b_lds[B_PER_T];
-  bool b_col_ok[B_PER_T];
-  int b_k[B_PER_T];
-#pragma unroll
-  for (int i = 0; i < B_PER_T; ++i) {
-    const int e = tid + kThreads * i;
-    const int r = e / B_CPR, c = e % B_CPR;
-    const int col = n0 + c * VB;
-    b_col_ok[i] = !CHECK || col < N;
-    const int col_c = (CHECK && col >= N) ? 0 : col;
-    b_k[i] = k_begin + r;
-    const int row_c = (CHECK && b_k[i] >= K) ? 0 : b_k[i];
-    pb[i] = B + (long long)row_c * N + col_c;
-    b_lds[i] = r * LDB + c * VB;
-  }
+  // Loads: thread tid takes chunk c = tid % CPR of row r0 = tid / CPR, then
+  // the same chunk of rows r0 + i * (T / CPR). One base pointer per operand;
+  // the per-load offsets are uniform across the workgroup.
+  constexpr int RA = T / A_CPR;   // A rows covered by one pass of the workgroup
+  constexpr int RB = T / B_CPR;   // B rows covered by one pass
+  static_assert(T % A_CPR == 0 && T % B_CPR == 0, "whole rows per pass");
+  const int ar0 = tid / A_CPR, ac = (tid % A_CPR) * VA;
+  const int br0 = tid / B_CPR, bc = (tid % B_CPR) * VB;
+  const float *pa = A + (long long)(m0 + ar0) * K + (k_begin + ac);
+  const float *pb = B + (long long)(k_begin + br0) * N + (n0 + bc);
+  const int a_lds = ar0 * LDA + ac;
+  const int b_lds = br0 * LDB + bc;
+  const bool b_col_ok = !CHECK || n0 + bc < N;
 
-  floatx4 ra[A_PER_T * VA / 4 + (VA == 1 ? 1 : 0)];
+  floatx4 ra[VA == 4 ? A_PER_T : 1];
   float ra1[VA == 1 ? A_PER_T : 1];
-  floatx4 rb[B_PER_T * VB / 4 + (VB == 1 ? 1 : 0)];
+  floatx4 rb[VB == 4 ? B_PER_T : 1];
   float rb1[VB == 1 ? B_PER_T : 1];
   (void)ra; (void)ra1; (void)rb; (void)rb1;
 
-  // Global -> registers for K step starting at k_off (relative to k_begin).
+  // Global -> registers for the K step starting at k_off (relative to k_begin).
   auto load_global = [&](int k_off) {
+    const bool a_k_ok = !CHECK || k_begin + ac + k_off < k_end;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      const bool ok = a_row_ok[i] && (!CHECK || a_k[i] + k_off < k_end);
+      const bool ok = a_k_ok && (!CHECK || m0 + ar0 + i * RA < M);
+      const float *p = pa + (long long)(i * RA) * K + k_off;
       if constexpr (VA == 4) {
-        ra[i] = ok ? *reinterpret_cast<const floatx4 *>(pa[i] + k_off) : floatx4{0.f, 0.f, 0.f, 0.f};
+        ra[i] = ok ? *reinterpret_cast<const floatx4 *>(p) : floatx4{0.f, 0.f, 0.f, 0.f};
       } else {
-        ra1[i] = ok ? pa[i][k_off] : 0.f;
+        ra1[i] = ok ? *p : 0.f;
       }
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
-      const bool ok = b_col_ok[i] && (!CHECK || b_k[i] + k_off < k_end);
-      const long long off = (long long)k_off * N;
+      const bool ok = b_col_ok && (!CHECK || k_begin + br0 + i * RB + k_off < k_end);
+      const float *p = pb + (long long)(i * RB + k_off) * N;
       if constexpr (VB == 4) {
-        rb[i] = ok ? *reinterpret_cast<const floatx4 *>(pb[i] + off) : floatx4{0.f, 0.f, 0.f, 0.f};
+        rb[i] = ok ? *reinterpret_cast<const floatx4 *>(p) : floatx4{0.f, 0.f, 0.f, 0.f};
       } else {
-        rb1[i] = ok ? pb[i][off] : 0.f;
+        rb1[i] = ok ? *p : 0.f;
       }
     }
   };
@@ -203,76 +235,115 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       if constexpr (VA == 4) {
-        *reinterpret_cast<floatx4 *>(&As[buf][a_lds[i]]) = ra[i];
+        *reinterpret_cast<floatx4 *>(&As[buf][a_lds + i * RA * LDA]) = ra[i];
       } else {
-        As[buf][a_lds[i]] = ra1[i];
+        As[buf][a_lds + i * RA * LDA] = ra1[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
       if constexpr (VB == 4) {
-        *reinterpret_cast<floatx4 *>(&Bs[buf][b_lds[i]]) = rb[i];
+        *reinterpret_cast<floatx4 *>(&Bs[buf][b_lds + i * RB * LDB]) = rb[i];
       } else {
-        Bs[buf][b_lds[i]] = rb1[i];
+        Bs[buf][b_lds + i * RB * LDB] = rb1[i];
       }
     }
   };
 
-  floatx16 acc[FM][FN];
+  // Fragments of one group (4 instructions): per block row of A one 16-byte
+  // read of 4 consecutive k; per block column of B 4 single reads.
+  floatx4 fa[2][FM];
+  float fb[2][FN][4];
+  const int a_frag_off = (wm * S::WM + li) * LDA + q * KS;
+  const int b_frag_off = (q * KS) * LDB + wn * S::WN + li;
+  auto load_frags = [&](int buf, int g, int slot) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(&As[buf][a_frag_off + fm * MI * LDA + 4 * g]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        fb[slot][fn][j] = Bs[buf][b_frag_off + (4 * g + j) * LDB + fn * MI];
+  };
+
+  acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      for (int v = 0; v < S::ACC; ++v) acc[i][j][v] = 0.0f;
 
+  auto mfma_step = [&](int slot, int j) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
+  };
+
+  // Prologue: K step 0 into buffer 0, its first fragments, K step 1 in flight.
   load_global(0);
   store_lds(0);
   __syncthreads();
+  load_frags(0, 0, 0);
+  if (nk > 1) load_global(BK);
 
-  for (int t = 0; t < nk; ++t) {
+  // One K step. The fragment slot of group g of step t is (t * NG + g) % 2;
+  // it must be a compile-time constant (registers cannot be indexed), so when
+  // NG is odd the step loop is unrolled by two and P = t % 2 is passed in.
+  auto k_step = [&](int t, auto parity) {
+    constexpr int P = decltype(parity)::value;
     const int cur = t & 1;
     const bool more = t + 1 < nk;
-    if (more) load_global((t + 1) * BK);
-
-    float a[FM][KH];
-    float b[FN][KH];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const float *src = &As[cur][(wm * S::WM + fm * 32 + l32) * LDA + half * KH];
+    for (int g = 0; g < NG; ++g) {
+      const int slot = (P * NG + g) & 1;
+      if (g < NG - 1) {
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, g + 1, slot ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < KH; s += 4) {
-        const floatx4 v = *reinterpret_cast<const floatx4 *>(src + s);
-        a[fm][s] = v[0]; a[fm][s + 1] = v[1]; a[fm][s + 2] = v[2]; a[fm][s + 3] = v[3];
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        if (more) store_lds(cur ^ 1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+          load_frags(cur ^ 1, 0, slot ^ 1);
+          if (t + 2 < nk) load_global((t + 2) * BK);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const float *src = &Bs[cur][(half * KH) * LDB + wn * S::WN + fn * 32 + l32];
-#pragma unroll
-      for (int s = 0; s < KH; ++s) b[fn][s] = src[s * LDB];
+  };
+  if constexpr (NG % 2 == 0) {
+    for (int t = 0; t < nk; ++t) k_step(t, std::integral_constant<int, 0>());
+  } else {
+    for (int t = 0; t < nk; t += 2) {
+      k_step(t, std::integral_constant<int, 0>());
+      if (t + 1 < nk) k_step(t + 1, std::integral_constant<int, 1>());
     }
-#pragma unroll
-    for (int s = 0; s < KH; ++s)
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][s], b[fn][s], acc[fm][fn], 0, 0, 0);
-
-    if (more) store_lds(cur ^ 1);
-    __syncthreads();
   }
 
-  // Epilogue: lane holds column l32 of each 32x32 block, rows 8*(v/4) + 4*half + v%4.
+  // Epilogue: accumulator v of block (fm, fn) is output row Op::row(q, v) and
+  // column li of that block.
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-      const int col = n0 + wn * S::WN + fn * 32 + l32;
+      const int col = n0 + wn * S::WN + fn * MI + li;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * S::WM + fm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      for (int v = 0; v < S::ACC; ++v) {
+        const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
         if (!CHECK || (row < M && col < N)) Cout[(long long)row * N + col] = acc[fm][fn][v];
       }
     }

@@ -59,14 +59,25 @@ enum {
 };
 
 /* Kernel identifiers for explicit plans. Tile = the BM x BN output block one
- * 256-thread workgroup computes. */
+ * workgroup computes, K step = the slice of K staged in LDS per barrier.
+ * "mfma32" kernels use v_mfma_f32_32x32x2_f32, "mfma16" kernels
+ * v_mfma_f32_16x16x4_f32; both are full FP32. */
 enum {
-  GEMM_KERNEL_AUTO = 0,          /* let the planner choose */
-  GEMM_KERNEL_MFMA_256x256 = 1,  /* FP32 MFMA 32x32x2, 4 waves of 128x128 */
-  GEMM_KERNEL_MFMA_256x128 = 2,  /* FP32 MFMA 32x32x2, 4 waves of 128x64 */
-  GEMM_KERNEL_MFMA_128x128 = 3,  /* FP32 MFMA 32x32x2, 4 waves of 64x64 */
-  GEMM_KERNEL_MFMA_64x64 = 4,    /* FP32 MFMA 32x32x2, 4 waves of 32x32 */
-  GEMM_KERNEL_VALU_64x64 = 10    /* vector-FMA kernel, 4x4 register tile per lane */
+  GEMM_KERNEL_AUTO = 0,            /* let the planner choose */
+  GEMM_KERNEL_MFMA_256x256 = 1,    /* mfma32, 256x256 tile, K step 16, 4 waves of 128x128 */
+  GEMM_KERNEL_MFMA_256x128 = 2,    /* mfma32, 256x128 tile, K step 16, 4 waves of 128x64 */
+  GEMM_KERNEL_MFMA_128x128 = 3,    /* mfma32, 128x128 tile, K step 16, 4 waves of 64x64 */
+  GEMM_KERNEL_MFMA_64x64 = 4,      /* mfma32, 64x64 tile, K step 16, 4 waves of 32x32 */
+  GEMM_KERNEL_MFMA_256x256_W8 = 5, /* mfma32, 256x256 tile, K step 16, 8 waves of 128x64 */
+  GEMM_KERNEL_VALU_64x64 = 10,     /* vector FMA, 64x64 tile, K step 16, 4x4 outputs per lane */
+  GEMM_KERNEL_MFMA16_256x256 = 11,    /* mfma16, 256x256 tile, K step 32, 4 waves of 128x128 */
+  GEMM_KERNEL_MFMA16_256x256_W8 = 12, /* mfma16, 256x256 tile, K step 32, 8 waves of 128x64 */
+  GEMM_KERNEL_MFMA16_256x128 = 13,    /* mfma16, 256x128 tile, K step 32, 4 waves of 128x64 */
+  GEMM_KERNEL_MFMA16_128x128 = 14,    /* mfma16, 128x128 tile, K step 32, 4 waves of 64x64 */
+  GEMM_KERNEL_MFMA16_64x64 = 15,      /* mfma16, 64x64 tile, K step 32, 4 waves of 32x32 */
+  GEMM_KERNEL_MFMA16_256x256_K16 = 16, /* mfma16, 256x256 tile, K step 16, 4 waves of 128x128 */
+  GEMM_KERNEL_MFMA16_128x128_K16 = 17, /* mfma16, 128x128 tile, K step 16, 4 waves of 64x64 */
+  GEMM_KERNEL_MFMA16_256x128_K16 = 18  /* mfma16, 256x128 tile, K step 16, 4 waves of 128x64 */
 };
 
 /* An execution plan: which kernel, and how many contiguous K ranges
