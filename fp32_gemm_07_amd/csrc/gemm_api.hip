@@ -45,7 +45,16 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_MFMA16_256x256_K16, 256, 256, 16, "mfma16_f32_256x256x16"},
     {GEMM_KERNEL_MFMA16_128x128_K16, 128, 128, 16, "mfma16_f32_128x128x16"},
     {GEMM_KERNEL_MFMA16_256x128_K16, 256, 128, 16, "mfma16_f32_256x128x16"},
+    {GEMM_KERNEL_MFMA_128x128_W1, 128, 128, 16, "mfma32_f32_128x128x16_w1"},
+    {GEMM_KERNEL_MFMA16_128x128_W1, 128, 128, 16, "mfma16_f32_128x128x16_w1"},
+    {GEMM_KERNEL_MFMA_64x64_W1, 64, 64, 16, "mfma32_f32_64x64x16_w1"},
     {GEMM_KERNEL_VALU_64x64, 64, 64, 16, "valu_f32_64x64x16"},
+    {GEMM_KERNEL_DMA32_256x256_W8, 256, 256, 16, "dma_mfma32_f32_256x256x16_w8_s4"},
+    {GEMM_KERNEL_DMA32_256x256_W4, 256, 256, 16, "dma_mfma32_f32_256x256x16_w4_s4"},
+    {GEMM_KERNEL_DMA16_256x256_W8, 256, 256, 16, "dma_mfma16_f32_256x256x16_w8_s4"},
+    {GEMM_KERNEL_DMA32_128x128_W4, 128, 128, 16, "dma_mfma32_f32_128x128x16_w4_s4"},
+    {GEMM_KERNEL_DMA16_128x128_W4, 128, 128, 16, "dma_mfma16_f32_128x128x16_w4_s4"},
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 256, 256, 16, "dma_mfma32_f32_256x256x16_w8_s3"},
 };
 
 const KernelInfo *find_kernel(int id) {
@@ -85,7 +94,8 @@ size_t workspace_for(int M, int N, const Resolved &r) {
 
 // The planner. Rules of thumb for one MI355X (256 CUs), from measured sweeps:
 //  - enough 256x256 tiles to give every CU one (>= 192): the 8-wave 256x256
-//    32x32x2 kernel, no split (134 TFLOP/s at 4096^3);
+//    32x32x2 kernel fed by direct global->LDS copies, no split (137 TFLOP/s
+//    at 4096^3; shapes it cannot take run the register-staged kernel);
 //  - few output tiles but a long K: split K until about 256 workgroups,
 //    keeping each K range >= 1024 (256x256 tiles for wide outputs, 128x128
 //    for narrow ones);
@@ -96,7 +106,7 @@ void plan(int M, int N, int K, int *kernel, int *split) {
   const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
   const long long t128 = ceil_div(M, 128) * ceil_div(N, 128);
   if (t256 >= 192) {
-    *kernel = GEMM_KERNEL_MFMA_256x256_W8;
+    *kernel = GEMM_KERNEL_DMA32_256x256_W8;
     return;
   }
   const long long kmin = 1024;
@@ -106,7 +116,7 @@ void plan(int M, int N, int K, int *kernel, int *split) {
     long long s = std::max<long long>(1, kNumCus / std::max<long long>(1, tiles));
     s = std::min<long long>(s, K / kmin);
     if (s > 1 || tiles >= 96) {
-      *kernel = wide ? GEMM_KERNEL_MFMA_256x256_W8 : GEMM_KERNEL_MFMA_128x128;
+      *kernel = wide ? GEMM_KERNEL_DMA32_256x256_W8 : GEMM_KERNEL_DMA32_128x128_W4;
       *split = static_cast<int>(s);
       return;
     }
@@ -210,6 +220,22 @@ bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K
   return false;
 }
 
+// Kernels fed by direct global -> LDS copies: 16-byte copies need K and N
+// multiples of 4 and 16-byte aligned A and B, and each lane's byte offset
+// within a tile (at most BM*K*4 for A, BK*N*4 for B) must stay below 2^31.
+// Returns false (nothing launched) for shapes outside that.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE>
+bool launch_dma(const float *A, const float *B, float *out, int M, int N, int K,
+                const Resolved &r, long long slab, hipStream_t stream) {
+  if (K % 4 != 0 || N % 4 != 0 || !aligned16(A) || !aligned16(B)) return false;
+  if ((long long)BM * K * 4 >= (1LL << 31) || (long long)BK * N * 4 >= (1LL << 31)) return false;
+  const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
+  hipLaunchKernelGGL((gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, WPE>), grid,
+                     dim3(64 * WAVES_M * WAVES_N), 0, stream, A, B, out, M, N, K, r.k_chunk,
+                     static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits, slab);
+  return true;
+}
+
 // Launch the kernel of r.k (falling back to a configuration with 4-byte
 // loads where the chosen one has none for this shape).
 void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N, int K,
@@ -255,6 +281,39 @@ void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N
       return;
     case GEMM_KERNEL_MFMA16_256x128_K16:
       launch_mfma<16, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA_128x128_W1:
+      launch_mfma<32, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA16_128x128_W1:
+      launch_mfma<16, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_MFMA_64x64_W1:
+      launch_mfma<32, 64, 64, 16, 1, 1, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA32_256x256_W8:
+      if (!launch_dma<32, 256, 256, 16, 2, 4, 4, 2>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA32_256x256_W8_S3:
+      if (!launch_dma<32, 256, 256, 16, 2, 4, 3, 2>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA32_256x256_W4:
+      if (!launch_dma<32, 256, 256, 16, 2, 2, 4, 1>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA16_256x256_W8:
+      if (!launch_dma<16, 256, 256, 16, 2, 4, 4, 2>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA32_128x128_W4:
+      if (!launch_dma<32, 128, 128, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA16_128x128_W4:
+      if (!launch_dma<16, 128, 128, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
       return;
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);

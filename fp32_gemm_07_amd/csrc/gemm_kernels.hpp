@@ -69,9 +69,12 @@ __device__ inline TileCoord map_tile(int bid, int tiles_m, int tiles_n, int spli
 // ---------------------------------------------------------------------------
 // FP32 MFMA kernel.
 //
-// BM x BN output tile per workgroup of 4 or 8 waves arranged WAVES_M x
+// BM x BN output tile per workgroup of 1, 2, 4 or 8 waves arranged WAVES_M x
 // WAVES_N; each wave owns a WM x WN sub-tile made of (WM/MI) x (WN/MI)
-// accumulator blocks of one FP32 matrix instruction:
+// accumulator blocks of one FP32 matrix instruction. With one wave per
+// workgroup the wave stages its own tiles and never waits on another wave
+// (the barrier of a one-wave workgroup is free), and several such workgroups
+// share a CU, one per SIMD.
 //   MI = 32: v_mfma_f32_32x32x2_f32 (32x2 by 2x32, 16 accumulators per lane);
 //   MI = 16: v_mfma_f32_16x16x4_f32 (16x4 by 4x16, 4 accumulators per lane).
 // Both retire 256 FLOP per clock per CU; on MI355X the chip holds a higher
@@ -112,7 +115,8 @@ struct MfmaShape {
   static constexpr int LDA = BK + 4;
   static constexpr int LDB = BN + 4;
   static_assert(MI == 16 || MI == 32, "16x16x4 or 32x32x2 FP32 MFMA");
-  static_assert(NWAVES == 4 || NWAVES == 8, "4 or 8 waves per workgroup");
+  static_assert(NWAVES == 1 || NWAVES == 2 || NWAVES == 4 || NWAVES == 8,
+                "1, 2, 4 or 8 waves per workgroup");
   static_assert(WM % MI == 0 && WN % MI == 0, "wave tile is whole blocks");
   static_assert(KS % 4 == 0 && (NG == 1 || NG % 2 == 0),
                 "K step is one or an even number of 4-instruction groups");
@@ -187,19 +191,29 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
   const int q = lane / MI;       // lane group: which k slot of each instruction
   const int li = lane % MI;      // row of A / column of B within a block
 
-  // Loads: thread tid takes chunk c = tid % CPR of row r0 = tid / CPR, then
-  // the same chunk of rows r0 + i * (T / CPR). One base pointer per operand;
-  // the per-load offsets are uniform across the workgroup.
-  constexpr int RA = T / A_CPR;   // A rows covered by one pass of the workgroup
-  constexpr int RB = T / B_CPR;   // B rows covered by one pass
-  static_assert(T % A_CPR == 0 && T % B_CPR == 0, "whole rows per pass");
-  const int ar0 = tid / A_CPR, ac = (tid % A_CPR) * VA;
-  const int br0 = tid / B_CPR, bc = (tid % B_CPR) * VB;
+  // Loads: the tile is CPR chunks (of VA or VB floats) per row; load i of
+  // thread tid takes chunk e = tid + T*i in row-major chunk order. Either a
+  // pass of the workgroup covers whole rows (T % CPR == 0: row r0 + i*T/CPR,
+  // fixed chunk) or a row takes several passes (CPR % T == 0: row i/(CPR/T),
+  // chunk tid + T*(i % (CPR/T))). Either way the per-load offsets from one
+  // base pointer per operand are uniform across the workgroup.
+  static_assert((T % A_CPR == 0 || A_CPR % T == 0) && (T % B_CPR == 0 || B_CPR % T == 0),
+                "load chunks tile the rows evenly");
+  constexpr bool A_WHOLE = T % A_CPR == 0, B_WHOLE = T % B_CPR == 0;
+  constexpr int A_RPP = A_WHOLE ? T / A_CPR : 1;   // rows per pass
+  constexpr int A_PPR = A_WHOLE ? 1 : A_CPR / T;   // passes per row
+  constexpr int B_RPP = B_WHOLE ? T / B_CPR : 1;
+  constexpr int B_PPR = B_WHOLE ? 1 : B_CPR / T;
+  auto a_row = [](int i) { return A_WHOLE ? i * A_RPP : i / A_PPR; };
+  auto a_col = [](int i) { return A_WHOLE ? 0 : T * (i % A_PPR) * VA; };
+  auto b_row = [](int i) { return B_WHOLE ? i * B_RPP : i / B_PPR; };
+  auto b_col = [](int i) { return B_WHOLE ? 0 : T * (i % B_PPR) * VB; };
+  const int ar0 = A_WHOLE ? tid / A_CPR : 0, ac = (A_WHOLE ? tid % A_CPR : tid) * VA;
+  const int br0 = B_WHOLE ? tid / B_CPR : 0, bc = (B_WHOLE ? tid % B_CPR : tid) * VB;
   const float *pa = A + (long long)(m0 + ar0) * K + (k_begin + ac);
   const float *pb = B + (long long)(k_begin + br0) * N + (n0 + bc);
   const int a_lds = ar0 * LDA + ac;
   const int b_lds = br0 * LDB + bc;
-  const bool b_col_ok = !CHECK || n0 + bc < N;
 
   floatx4 ra[VA == 4 ? A_PER_T : 1];
   float ra1[VA == 1 ? A_PER_T : 1];
@@ -209,11 +223,10 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 
   // Global -> registers for the K step starting at k_off (relative to k_begin).
   auto load_global = [&](int k_off) {
-    const bool a_k_ok = !CHECK || k_begin + ac + k_off < k_end;
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      const bool ok = a_k_ok && (!CHECK || m0 + ar0 + i * RA < M);
-      const float *p = pa + (long long)(i * RA) * K + k_off;
+      const bool ok = !CHECK || (k_begin + ac + a_col(i) + k_off < k_end && m0 + ar0 + a_row(i) < M);
+      const float *p = pa + (long long)a_row(i) * K + a_col(i) + k_off;
       if constexpr (VA == 4) {
         ra[i] = ok ? *reinterpret_cast<const floatx4 *>(p) : floatx4{0.f, 0.f, 0.f, 0.f};
       } else {
@@ -222,8 +235,9 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
-      const bool ok = b_col_ok && (!CHECK || k_begin + br0 + i * RB + k_off < k_end);
-      const float *p = pb + (long long)(i * RB + k_off) * N;
+      const bool ok =
+          !CHECK || (n0 + bc + b_col(i) < N && k_begin + br0 + b_row(i) + k_off < k_end);
+      const float *p = pb + (long long)(b_row(i) + k_off) * N + b_col(i);
       if constexpr (VB == 4) {
         rb[i] = ok ? *reinterpret_cast<const floatx4 *>(p) : floatx4{0.f, 0.f, 0.f, 0.f};
       } else {
@@ -234,18 +248,20 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
   auto store_lds = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
+      const int off = a_lds + a_row(i) * LDA + a_col(i);
       if constexpr (VA == 4) {
-        *reinterpret_cast<floatx4 *>(&As[buf][a_lds + i * RA * LDA]) = ra[i];
+        *reinterpret_cast<floatx4 *>(&As[buf][off]) = ra[i];
       } else {
-        As[buf][a_lds + i * RA * LDA] = ra1[i];
+        As[buf][off] = ra1[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) {
+      const int off = b_lds + b_row(i) * LDB + b_col(i);
       if constexpr (VB == 4) {
-        *reinterpret_cast<floatx4 *>(&Bs[buf][b_lds + i * RB * LDB]) = rb[i];
+        *reinterpret_cast<floatx4 *>(&Bs[buf][off]) = rb[i];
       } else {
-        Bs[buf][b_lds + i * RB * LDB] = rb1[i];
+        Bs[buf][off] = rb1[i];
       }
     }
   };
@@ -345,6 +361,284 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
       for (int v = 0; v < S::ACC; ++v) {
         const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
         if (!CHECK || (row < M && col < N)) Cout[(long long)row * N + col] = acc[fm][fn][v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// FP32 MFMA kernel fed by direct global -> LDS loads.
+//
+// gfx950's buffer_load_dwordx4 ... lds copies 16 bytes per lane from global
+// memory straight into LDS (lane i's bytes land at M0 + 16*i), so no data
+// passes through registers: no staging VGPRs, no LDS store instructions, and
+// the wave only waits for a K step's data when it is about to consume it.
+// K steps rotate through NS LDS stages: while step t is being multiplied,
+// steps t+1 .. t+NS-1 are in flight. Each lane's load goes through a buffer
+// resource whose range check turns an out-of-range offset into zeros; lanes
+// whose chunk lies past M, N or the end of the K range get such an offset,
+// which is the zero fill of the edges.
+//
+// Because a copy lands in LDS exactly as the 64 lanes are ordered, rows
+// cannot be padded; instead 16-byte chunks are XOR-swizzled within a row:
+//   A [BM][BK] : chunk c of row r is stored at chunk c ^ swz_a(r), chosen
+//                so that the 16-byte fragment reads of 16 consecutive rows
+//                hit distinct banks;
+//   B [BK][BN] : chunk c of row k is stored at chunk c ^ swb(k),
+//                swb(k) = ((k / KS) % NQ) * (MI / 4), so the NQ lane groups of
+//                an instruction, which read rows KS apart, land MI floats
+//                apart, on different banks.
+// The copies are issued with inline assembly: the compiler does not model
+// the LDS write of its own builtin for this instruction, so the asm carries
+// a memory clobber and the waits (s_waitcnt vmcnt) are explicit.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x4 make_buffer_rsrc(const void *base) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  u32x4 r;
+  r[0] = static_cast<unsigned>(a);
+  r[1] = static_cast<unsigned>(a >> 32) & 0xffffu;  // stride 0: raw byte buffer
+  r[2] = 0x80000000u;                               // range: offsets below 2^31
+  r[3] = 0x00020000u;                               // 32-bit data, raw access
+  return r;
+}
+constexpr unsigned kOutOfRange = 0x80000000u;
+
+__device__ inline void dma_16B(const u32x4 &rsrc, unsigned voffset, unsigned lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte_addr), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS>
+struct DmaShape {
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int NQ = 64 / MI;
+  static constexpr int ACC = MI * MI / 64;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int FM = WM / MI, FN = WN / MI;
+  static constexpr int KS = BK / NQ;
+  static constexpr int NG = KS / 4;
+  static constexpr int CPA = BK / 4;          // 16-byte chunks per A row
+  static constexpr int RPA = 64 / CPA;        // A rows per copy instruction
+  static constexpr int IA = BM / RPA;         // A copy instructions per stage
+  static constexpr int CPB = BN / 4;          // chunks per B row
+  static constexpr int RPB = 64 / CPB;        // B rows per copy instruction
+  static constexpr int IB = BK / RPB;         // B copy instructions per stage
+  static constexpr int LPW = (IA + IB) / NWAVES;  // copies per wave per stage
+  static constexpr int A_BYTES = BM * BK * 4;
+  static constexpr int STAGE_BYTES = (BM * BK + BK * BN) * 4;
+  static_assert(CPA == 4 || CPA == 8, "K step of 16 or 32");
+  static_assert(CPB >= 16 && CPB <= 64 && 64 % CPB == 0, "B rows of 64 to 256 floats");
+  static_assert((IA + IB) % NWAVES == 0 && IA % NWAVES == 0, "copies split evenly over waves");
+  static_assert(KS % 4 == 0 && (NG == 1 || NG % 2 == 0), "fragment groups");
+  static_assert(NS >= 3 && NS <= 4, "3 or 4 stages");
+  static_assert(NS * STAGE_BYTES <= 160 * 1024, "fits LDS");
+  static_assert((NS - 1) * LPW < 64, "vmcnt range");
+};
+
+// Swizzle of A rows: with 4 chunks per row (BK = 16) 16 consecutive rows are
+// told apart by r % 4 (bank quarter) and (r / 4) % 4 (chunk); with 8 chunks
+// per row (BK = 32) by r % 2 and (r / 2) % 8.
+template <int CPA>
+__device__ inline int swz_a(int r) {
+  return CPA == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
+                                                      64 * WAVES_M * WAVES_N),
+                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
+                          float *__restrict__ C, int M, int N, int K, int k_chunk,
+                          int tiles_m, int tiles_n, int splits, long long slab) {
+  using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS>;
+  using Op = Mfma<MI>;
+  using acc_t = typename Op::acc_t;
+  constexpr int FM = S::FM, FN = S::FN, KS = S::KS, NG = S::NG, NQ = S::NQ;
+  constexpr int CPA = S::CPA, RPA = S::RPA, IA = S::IA, CPB = S::CPB, RPB = S::RPB;
+  constexpr int LPW = S::LPW, NW = S::NWAVES;
+
+  __shared__ __attribute__((aligned(16))) float smem[NS * S::STAGE_BYTES / 4];
+  // One real store into the shared array, so the compiler cannot treat it as
+  // never written (the copies write it behind the compiler's back).
+  if (threadIdx.x == 0) smem[0] = 0.0f;
+
+  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, 8);
+  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+  const int k_begin = tc.split * k_chunk;
+  const int k_end = min(K, k_begin + k_chunk);
+  const int nk = (k_end - k_begin + BK - 1) / BK;
+  float *__restrict__ Cout = C + (long long)tc.split * slab;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int q = lane / MI;
+  const int li = lane % MI;
+  const unsigned smem_base =
+      static_cast<unsigned>(reinterpret_cast<unsigned long long>(
+          (__attribute__((address_space(3))) float *)smem));
+
+  // Copy instructions of this wave: n = wave + NW * i over the IA A copies
+  // then the IB B copies of a stage. Per instruction, this lane's byte
+  // offset from the K step's base and its validity apart from the K range.
+  unsigned cp_off[LPW];
+  unsigned cp_lds[LPW];
+  int cp_k[LPW];       // A: the lane's first k within the step; B: its k row
+  bool cp_ok[LPW];     // row (A) or column (B) inside the matrix
+  bool cp_is_a[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int n = wave + NW * i;
+    if (n < IA) {
+      const int r = n * RPA + lane / CPA;
+      const int pc = lane % CPA;
+      const int lc = pc ^ swz_a<CPA>(r);
+      cp_is_a[i] = true;
+      cp_ok[i] = m0 + r < M;
+      cp_k[i] = 4 * lc;
+      cp_off[i] = (static_cast<unsigned>(r) * static_cast<unsigned>(K) + 4u * lc) * 4u;
+      cp_lds[i] = static_cast<unsigned>(n) * 1024u;
+    } else {
+      const int nb = n - IA;
+      const int k = nb * RPB + lane / CPB;
+      const int pc = lane % CPB;
+      const int lc = pc ^ (((k / KS) % NQ) * (MI / 4));
+      cp_is_a[i] = false;
+      cp_ok[i] = n0 + 4 * lc < N;
+      cp_k[i] = k;
+      cp_off[i] = (static_cast<unsigned>(k) * static_cast<unsigned>(N) + 4u * lc) * 4u;
+      cp_lds[i] = S::A_BYTES + static_cast<unsigned>(nb) * 1024u;
+    }
+  }
+  // Issue the copies of K step `step` into its stage.
+  auto issue = [&](int step) {
+    const int k0 = k_begin + step * BK;
+    const u32x4 ra = make_buffer_rsrc(A + (long long)m0 * K + k0);
+    const u32x4 rb = make_buffer_rsrc(B + (long long)k0 * N + n0);
+    const unsigned stage = smem_base + static_cast<unsigned>((step % NS) * S::STAGE_BYTES);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const bool ok = cp_ok[i] && (k0 + cp_k[i] < k_end);
+      dma_16B(cp_is_a[i] ? ra : rb, ok ? cp_off[i] : kOutOfRange, stage + cp_lds[i]);
+    }
+  };
+  // Wait until this wave's copies of a step have landed while the copies of
+  // `later` steps issued after it may stay in flight (vmcnt counts this
+  // wave's outstanding copies, oldest first).
+  auto wait_landed = [&](int later) {
+    if constexpr (NS >= 4) {
+      if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
+    }
+    if (later >= 1) { wait_vmcnt<LPW>(); return; }
+    wait_vmcnt<0>();
+  };
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
+
+  // Fragment reads (swizzled addresses), as in mfma_gemm_kernel.
+  floatx4 fa[2][FM];
+  float fb[2][FN][4];
+  auto load_frags = [&](int step, int g, int slot) {
+    const float *st = smem + (step % NS) * (S::STAGE_BYTES / 4);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = wm * S::WM + fm * MI + li;
+      const int lc = (q * KS + 4 * g) / 4;
+      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(st + r * BK + 4 * (lc ^ swz_a<CPA>(r)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = q * KS + 4 * g + j;
+      const int flip = ((k / KS) % NQ) * MI;   // column flip of row k, in floats
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int n = (wn * S::WN + fn * MI + li) ^ flip;
+        fb[slot][fn][j] = st[BM * BK + k * BN + n];
+      }
+    }
+  };
+
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < S::ACC; ++v) acc[i][j][v] = 0.0f;
+  auto mfma_step = [&](int slot, int j) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
+  };
+
+  // Prologue: steps 0 .. NS-2 in flight, step 0 landed, its first fragments.
+  barrier();  // the store into smem[0] precedes every copy
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s);
+  wait_landed(min(NS - 2, nk - 1));
+  barrier();
+  load_frags(0, 0, 0);
+
+  auto k_step = [&](int t, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    const bool more = t + 1 < nk;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int slot = (P * NG + g) & 1;
+      if (g < NG - 1) {
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(t, g + 1, slot ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // Steps up to t+NS-2 have been issued. Step t+1 has landed once every
+        // wave has waited for it (the later ones may stay in flight), and
+        // every read of step t-1's stage finished before the previous barrier,
+        // so after this barrier step t+NS-1 can be copied into that stage.
+        if (more) wait_landed(min(NS - 3, nk - 2 - t));
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) load_frags(t + 1, 0, slot ^ 1);
+        if (t + NS - 1 < nk) issue(t + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  for (int t = 0; t < nk; t += 2) {
+    k_step(t, std::integral_constant<int, 0>());
+    if (t + 1 < nk) k_step(t + 1, std::integral_constant<int, 1>());
+  }
+
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = n0 + wn * S::WN + fn * MI + li;
+#pragma unroll
+      for (int v = 0; v < S::ACC; ++v) {
+        const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
+        if (row < M && col < N) Cout[(long long)row * N + col] = acc[fm][fn][v];
       }
     }
   }

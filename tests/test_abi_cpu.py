@@ -98,7 +98,7 @@ def test_invalid_plans_rejected():
 
 def test_planner_choices_for_standing_workloads():
     p4 = binding.gemm_f32_plan(4096, 4096, 4096)
-    assert p4.kernel == binding.GEMM_KERNEL_MFMA_256x256_W8 and p4.split_k == 1
+    assert p4.kernel == binding.GEMM_KERNEL_DMA32_256x256_W8 and p4.split_k == 1
     p5 = binding.gemm_f32_plan(512, 512, 131072)
     assert p5.split_k > 1 and p5.k_chunk * p5.split_k >= 131072
     assert p5.k_chunk % 16 == 0
