@@ -43,11 +43,13 @@ GEMM_KERNEL_MFMA_128x128_W1 = 19
 GEMM_KERNEL_MFMA16_128x128_W1 = 20
 GEMM_KERNEL_MFMA_64x64_W1 = 21
 GEMM_KERNEL_DMA32_256x256_W8 = 30
-GEMM_KERNEL_DMA32_256x256_W4 = 31
 GEMM_KERNEL_DMA16_256x256_W8 = 32
 GEMM_KERNEL_DMA32_128x128_W4 = 33
 GEMM_KERNEL_DMA16_128x128_W4 = 34
 GEMM_KERNEL_DMA32_256x256_W8_S3 = 35
+GEMM_KERNEL_DMA16_64x64 = 36
+GEMM_KERNEL_DMA32_64x64 = 37
+GEMM_KERNEL_DMA16_128x64 = 38
 
 KERNELS = {
     "mfma32_256x256": GEMM_KERNEL_MFMA_256x256,
@@ -67,11 +69,13 @@ KERNELS = {
     "mfma16_128x128_w1": GEMM_KERNEL_MFMA16_128x128_W1,
     "mfma32_64x64_w1": GEMM_KERNEL_MFMA_64x64_W1,
     "dma32_256x256_w8": GEMM_KERNEL_DMA32_256x256_W8,
-    "dma32_256x256_w4": GEMM_KERNEL_DMA32_256x256_W4,
     "dma16_256x256_w8": GEMM_KERNEL_DMA16_256x256_W8,
     "dma32_128x128_w4": GEMM_KERNEL_DMA32_128x128_W4,
     "dma16_128x128_w4": GEMM_KERNEL_DMA16_128x128_W4,
     "dma32_256x256_w8_s3": GEMM_KERNEL_DMA32_256x256_W8_S3,
+    "dma16_64x64": GEMM_KERNEL_DMA16_64x64,
+    "dma32_64x64": GEMM_KERNEL_DMA32_64x64,
+    "dma16_128x64": GEMM_KERNEL_DMA16_128x64,
     "valu_64x64": GEMM_KERNEL_VALU_64x64,
 }
 

@@ -50,11 +50,13 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_MFMA_64x64_W1, 64, 64, 16, "mfma32_f32_64x64x16_w1"},
     {GEMM_KERNEL_VALU_64x64, 64, 64, 16, "valu_f32_64x64x16"},
     {GEMM_KERNEL_DMA32_256x256_W8, 256, 256, 16, "dma_mfma32_f32_256x256x16_w8_s4"},
-    {GEMM_KERNEL_DMA32_256x256_W4, 256, 256, 16, "dma_mfma32_f32_256x256x16_w4_s4"},
     {GEMM_KERNEL_DMA16_256x256_W8, 256, 256, 16, "dma_mfma16_f32_256x256x16_w8_s4"},
     {GEMM_KERNEL_DMA32_128x128_W4, 128, 128, 16, "dma_mfma32_f32_128x128x16_w4_s4"},
     {GEMM_KERNEL_DMA16_128x128_W4, 128, 128, 16, "dma_mfma16_f32_128x128x16_w4_s4"},
     {GEMM_KERNEL_DMA32_256x256_W8_S3, 256, 256, 16, "dma_mfma32_f32_256x256x16_w8_s3"},
+    {GEMM_KERNEL_DMA16_64x64, 64, 64, 32, "dma_mfma16_f32_64x64x32_w4_s4"},
+    {GEMM_KERNEL_DMA32_64x64, 64, 64, 16, "dma_mfma32_f32_64x64x16_w4_s4"},
+    {GEMM_KERNEL_DMA16_128x64, 128, 64, 32, "dma_mfma16_f32_128x64x32_w4_s4"},
 };
 
 const KernelInfo *find_kernel(int id) {
@@ -100,7 +102,7 @@ size_t workspace_for(int M, int N, const Resolved &r) {
 //    keeping each K range >= 1024 (256x256 tiles for wide outputs, 128x128
 //    for narrow ones);
 //  - otherwise 64x64 tiles of the 16x16x4 kernel (one workgroup per CU at
-//    1024x1024 outputs).
+//    1024x1024 outputs), copy-fed when K or N is not a multiple of 4.
 void plan(int M, int N, int K, int *kernel, int *split) {
   *split = 1;
   const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
@@ -125,7 +127,9 @@ void plan(int M, int N, int K, int *kernel, int *split) {
     *kernel = GEMM_KERNEL_MFMA_128x128;
     return;
   }
-  *kernel = GEMM_KERNEL_MFMA16_64x64;
+  // Rows that are not a whole number of 16-byte chunks: the copy-fed kernel's
+  // 16-byte copies beat the register-staged kernel's 4-byte loads.
+  *kernel = (K % 4 != 0 || N % 4 != 0) ? GEMM_KERNEL_DMA16_64x64 : GEMM_KERNEL_MFMA16_64x64;
 }
 
 // ---------------------------------------------------------------------------
@@ -220,19 +224,19 @@ bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K
   return false;
 }
 
-// Kernels fed by direct global -> LDS copies: 16-byte copies need K and N
-// multiples of 4 and 16-byte aligned A and B, and each lane's byte offset
-// within a tile (at most BM*K*4 for A, BK*N*4 for B) must stay below 2^31.
-// Returns false (nothing launched) for shapes outside that.
+// Kernels fed by direct global -> LDS copies (16-byte copies from 4-byte
+// aligned sources, any K and N). Each lane's byte offset within a tile (at
+// most BM*K*4 for A, BK*N*4 for B) must stay below 2^31; returns false
+// (nothing launched) for shapes outside that.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE>
 bool launch_dma(const float *A, const float *B, float *out, int M, int N, int K,
                 const Resolved &r, long long slab, hipStream_t stream) {
-  if (K % 4 != 0 || N % 4 != 0 || !aligned16(A) || !aligned16(B)) return false;
   if ((long long)BM * K * 4 >= (1LL << 31) || (long long)BK * N * 4 >= (1LL << 31)) return false;
   const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
-  hipLaunchKernelGGL((gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, WPE>), grid,
-                     dim3(64 * WAVES_M * WAVES_N), 0, stream, A, B, out, M, N, K, r.k_chunk,
-                     static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits, slab);
+  hipLaunchKernelGGL((gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE>),
+                     grid, dim3(64 * WAVES_M * WAVES_N), 0, stream, A, B, out, M, N, K,
+                     r.k_chunk, static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n),
+                     r.splits, slab);
   return true;
 }
 
@@ -299,10 +303,6 @@ void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N
       if (!launch_dma<32, 256, 256, 16, 2, 4, 3, 2>(A, B, out, M, N, K, r, slab, stream))
         launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
       return;
-    case GEMM_KERNEL_DMA32_256x256_W4:
-      if (!launch_dma<32, 256, 256, 16, 2, 2, 4, 1>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
     case GEMM_KERNEL_DMA16_256x256_W8:
       if (!launch_dma<16, 256, 256, 16, 2, 4, 4, 2>(A, B, out, M, N, K, r, slab, stream))
         launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
@@ -314,6 +314,18 @@ void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N
     case GEMM_KERNEL_DMA16_128x128_W4:
       if (!launch_dma<16, 128, 128, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream))
         launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA16_64x64:
+      launch_dma<16, 64, 64, 32, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream) ||
+          launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA32_64x64:
+      launch_dma<32, 64, 64, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream) ||
+          launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      return;
+    case GEMM_KERNEL_DMA16_128x64:
+      launch_dma<16, 128, 64, 32, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream) ||
+          launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
       return;
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);

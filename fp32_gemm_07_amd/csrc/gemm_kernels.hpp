@@ -370,14 +370,19 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 // FP32 MFMA kernel fed by direct global -> LDS loads.
 //
 // gfx950's buffer_load_dwordx4 ... lds copies 16 bytes per lane from global
-// memory straight into LDS (lane i's bytes land at M0 + 16*i), so no data
+// memory straight into LDS (lane i's bytes land at M0 + 16*i; the 4-byte
+// form buffer_load_dword ... lds puts lane i's float at M0 + 4*i), so no data
 // passes through registers: no staging VGPRs, no LDS store instructions, and
 // the wave only waits for a K step's data when it is about to consume it.
 // K steps rotate through NS LDS stages: while step t is being multiplied,
-// steps t+1 .. t+NS-1 are in flight. Each lane's load goes through a buffer
+// steps t+1 .. t+NS-2 are in flight. Each lane's load goes through a buffer
 // resource whose range check turns an out-of-range offset into zeros; lanes
 // whose chunk lies past M, N or the end of the K range get such an offset,
-// which is the zero fill of the edges.
+// which is the zero fill of the edges. The 16-byte copies only need 4-byte
+// aligned sources, so rows of any length are copied this way; a chunk that
+// straddles the end of the K range has its trailing floats zeroed in LDS
+// (zero_k_tail), and chunks straddling the last column of B only feed
+// outputs past N, which are never stored.
 //
 // Because a copy lands in LDS exactly as the 64 lanes are ordered, rows
 // cannot be padded; instead 16-byte chunks are XOR-swizzled within a row:
@@ -393,22 +398,35 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 // a memory clobber and the waits (s_waitcnt vmcnt) are explicit.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline u32x4 make_buffer_rsrc(const void *base) {
+// Raw buffer resource: base address, byte range [0, bytes) (each dword of a
+// load is checked on its own: dwords at or past the range read as zero), 32-bit
+// data. bytes is capped at 2^31 so that kOutOfRange is always past the range.
+__device__ inline u32x4 make_buffer_rsrc(const void *base, long long bytes) {
   const unsigned long long a = reinterpret_cast<unsigned long long>(base);
   u32x4 r;
   r[0] = static_cast<unsigned>(a);
   r[1] = static_cast<unsigned>(a >> 32) & 0xffffu;  // stride 0: raw byte buffer
-  r[2] = 0x80000000u;                               // range: offsets below 2^31
+  r[2] = static_cast<unsigned>(bytes < 0 ? 0 : (bytes > 0x80000000LL ? 0x80000000LL : bytes));
   r[3] = 0x00020000u;                               // 32-bit data, raw access
   return r;
 }
 constexpr unsigned kOutOfRange = 0x80000000u;
 
-__device__ inline void dma_16B(const u32x4 &rsrc, unsigned voffset, unsigned lds_byte_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_byte_addr), "v"(voffset), "s"(rsrc)
-               : "memory");
+// One copy instruction: each lane moves VEC floats (16 or 4 bytes) from
+// rsrc + voffset into LDS at lds_byte_addr + lane * 4 * VEC.
+template <int VEC>
+__device__ inline void dma_copy(const u32x4 &rsrc, unsigned voffset, unsigned lds_byte_addr) {
+  if constexpr (VEC == 4) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_byte_addr), "v"(voffset), "s"(rsrc)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_byte_addr), "v"(voffset), "s"(rsrc)
+                 : "memory");
+  }
 }
 
 template <int N>
@@ -417,7 +435,7 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC>
 struct DmaShape {
   static constexpr int NWAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * NWAVES;
@@ -427,44 +445,49 @@ struct DmaShape {
   static constexpr int FM = WM / MI, FN = WN / MI;
   static constexpr int KS = BK / NQ;
   static constexpr int NG = KS / 4;
-  static constexpr int CPA = BK / 4;          // 16-byte chunks per A row
-  static constexpr int RPA = 64 / CPA;        // A rows per copy instruction
+  static constexpr int CA = BK / 4;           // 16-byte chunks per A row (swizzle unit)
+  static constexpr int EPA = BK / VEC;        // copy elements (lanes) per A row
+  static constexpr int RPA = 64 / EPA;        // A rows per copy instruction
   static constexpr int IA = BM / RPA;         // A copy instructions per stage
-  static constexpr int CPB = BN / 4;          // chunks per B row
-  static constexpr int RPB = 64 / CPB;        // B rows per copy instruction
+  static constexpr int EPB = BN / VEC;        // copy elements per B row
+  static constexpr int RPB = 64 / EPB;        // B rows per copy instruction
   static constexpr int IB = BK / RPB;         // B copy instructions per stage
   static constexpr int LPW = (IA + IB) / NWAVES;  // copies per wave per stage
+  static constexpr int COPY_BYTES = 256 * VEC;    // LDS bytes one copy instruction fills
   static constexpr int A_BYTES = BM * BK * 4;
   static constexpr int STAGE_BYTES = (BM * BK + BK * BN) * 4;
-  static_assert(CPA == 4 || CPA == 8, "K step of 16 or 32");
-  static_assert(CPB >= 16 && CPB <= 64 && 64 % CPB == 0, "B rows of 64 to 256 floats");
+  static_assert(VEC == 4 || VEC == 1, "16- or 4-byte copies");
+  static_assert(CA == 4 || CA == 8, "K step of 16 or 32");
+  static_assert(EPA <= 64 && 64 % EPA == 0, "whole A rows per copy");
+  static_assert(EPB <= 64 && 64 % EPB == 0 && BN >= 64, "whole B rows per copy");
   static_assert((IA + IB) % NWAVES == 0 && IA % NWAVES == 0, "copies split evenly over waves");
   static_assert(KS % 4 == 0 && (NG == 1 || NG % 2 == 0), "fragment groups");
   static_assert(NS >= 3 && NS <= 4, "3 or 4 stages");
   static_assert(NS * STAGE_BYTES <= 160 * 1024, "fits LDS");
-  static_assert((NS - 1) * LPW < 64, "vmcnt range");
+  static_assert((NS - 2) * LPW < 64, "vmcnt wait values fit the counter");
 };
 
 // Swizzle of A rows: with 4 chunks per row (BK = 16) 16 consecutive rows are
 // told apart by r % 4 (bank quarter) and (r / 4) % 4 (chunk); with 8 chunks
 // per row (BK = 32) by r % 2 and (r / 2) % 8.
-template <int CPA>
+template <int CA>
 __device__ inline int swz_a(int r) {
-  return CPA == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+  return CA == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WAVES_PER_EU>
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC,
+          int WAVES_PER_EU>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
                           float *__restrict__ C, int M, int N, int K, int k_chunk,
                           int tiles_m, int tiles_n, int splits, long long slab) {
-  using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS>;
+  using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, VEC>;
   using Op = Mfma<MI>;
   using acc_t = typename Op::acc_t;
   constexpr int FM = S::FM, FN = S::FN, KS = S::KS, NG = S::NG, NQ = S::NQ;
-  constexpr int CPA = S::CPA, RPA = S::RPA, IA = S::IA, CPB = S::CPB, RPB = S::RPB;
+  constexpr int CA = S::CA, EPA = S::EPA, RPA = S::RPA, IA = S::IA, EPB = S::EPB, RPB = S::RPB;
   constexpr int LPW = S::LPW, NW = S::NWAVES;
 
   __shared__ __attribute__((aligned(16))) float smem[NS * S::STAGE_BYTES / 4];
@@ -501,36 +524,42 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   for (int i = 0; i < LPW; ++i) {
     const int n = wave + NW * i;
     if (n < IA) {
-      const int r = n * RPA + lane / CPA;
-      const int pc = lane % CPA;
-      const int lc = pc ^ swz_a<CPA>(r);
+      // lane -> row r, physical float pe of that row; logical float ke
+      const int r = n * RPA + lane / EPA;
+      const int pe = (lane % EPA) * VEC;
+      const int ke = ((pe / 4) ^ swz_a<CA>(r)) * 4 + pe % 4;
       cp_is_a[i] = true;
       cp_ok[i] = m0 + r < M;
-      cp_k[i] = 4 * lc;
-      cp_off[i] = (static_cast<unsigned>(r) * static_cast<unsigned>(K) + 4u * lc) * 4u;
-      cp_lds[i] = static_cast<unsigned>(n) * 1024u;
+      cp_k[i] = ke;
+      cp_off[i] = (static_cast<unsigned>(r) * static_cast<unsigned>(K) + ke) * 4u;
+      cp_lds[i] = static_cast<unsigned>(n * S::COPY_BYTES);
     } else {
       const int nb = n - IA;
-      const int k = nb * RPB + lane / CPB;
-      const int pc = lane % CPB;
-      const int lc = pc ^ (((k / KS) % NQ) * (MI / 4));
+      const int k = nb * RPB + lane / EPB;
+      const int pe = (lane % EPB) * VEC;
+      const int ne = pe ^ (((k / KS) % NQ) * MI);
       cp_is_a[i] = false;
-      cp_ok[i] = n0 + 4 * lc < N;
+      cp_ok[i] = n0 + ne < N;
       cp_k[i] = k;
-      cp_off[i] = (static_cast<unsigned>(k) * static_cast<unsigned>(N) + 4u * lc) * 4u;
-      cp_lds[i] = S::A_BYTES + static_cast<unsigned>(nb) * 1024u;
+      cp_off[i] = (static_cast<unsigned>(k) * static_cast<unsigned>(N) + ne) * 4u;
+      cp_lds[i] = static_cast<unsigned>(S::A_BYTES + nb * S::COPY_BYTES);
     }
   }
   // Issue the copies of K step `step` into its stage.
+  // The ranges end exactly at the end of A and of B, so a chunk that runs
+  // past the last element of the matrix reads zeros there instead of memory
+  // beyond the allocation.
+  const long long a_elems = (long long)M * K, b_elems = (long long)K * N;
   auto issue = [&](int step) {
     const int k0 = k_begin + step * BK;
-    const u32x4 ra = make_buffer_rsrc(A + (long long)m0 * K + k0);
-    const u32x4 rb = make_buffer_rsrc(B + (long long)k0 * N + n0);
+    const long long a_first = (long long)m0 * K + k0, b_first = (long long)k0 * N + n0;
+    const u32x4 ra = make_buffer_rsrc(A + a_first, 4 * (a_elems - a_first));
+    const u32x4 rb = make_buffer_rsrc(B + b_first, 4 * (b_elems - b_first));
     const unsigned stage = smem_base + static_cast<unsigned>((step % NS) * S::STAGE_BYTES);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const bool ok = cp_ok[i] && (k0 + cp_k[i] < k_end);
-      dma_16B(cp_is_a[i] ? ra : rb, ok ? cp_off[i] : kOutOfRange, stage + cp_lds[i]);
+      dma_copy<VEC>(cp_is_a[i] ? ra : rb, ok ? cp_off[i] : kOutOfRange, stage + cp_lds[i]);
     }
   };
   // Wait until this wave's copies of a step have landed while the copies of
@@ -544,6 +573,25 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     wait_vmcnt<0>();
   };
   auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
+  // When the K range does not end on a 16-byte chunk, the A chunk of each
+  // row that straddles its end also brought in up to three floats past it
+  // (the start of the next row). Once this wave's copies of the last step
+  // have landed, it zeroes those floats in the chunks it copied itself.
+  auto zero_k_tail = [&](int step) {
+    if constexpr (VEC == 4) {
+      const int k0 = k_begin + step * BK;
+      if (step != nk - 1 || (k_end - k0) % 4 == 0) return;
+      const int stage_f = (step % NS) * (S::STAGE_BYTES / 4);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int ks = k0 + cp_k[i];
+        if (cp_is_a[i] && cp_ok[i] && ks < k_end && ks + 4 > k_end) {
+          float *dst = smem + stage_f + cp_lds[i] / 4 + lane * 4;
+          for (int e = k_end - ks; e < 4; ++e) dst[e] = 0.0f;
+        }
+      }
+    }
+  };
 
   // Fragment reads (swizzled addresses), as in mfma_gemm_kernel.
   floatx4 fa[2][FM];
@@ -554,7 +602,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     for (int fm = 0; fm < FM; ++fm) {
       const int r = wm * S::WM + fm * MI + li;
       const int lc = (q * KS + 4 * g) / 4;
-      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(st + r * BK + 4 * (lc ^ swz_a<CPA>(r)));
+      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(st + r * BK + 4 * (lc ^ swz_a<CA>(r)));
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -589,6 +637,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue(s);
   wait_landed(min(NS - 2, nk - 1));
+  zero_k_tail(0);
   barrier();
   load_frags(0, 0, 0);
 
@@ -611,7 +660,10 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         // wave has waited for it (the later ones may stay in flight), and
         // every read of step t-1's stage finished before the previous barrier,
         // so after this barrier step t+NS-1 can be copied into that stage.
-        if (more) wait_landed(min(NS - 3, nk - 2 - t));
+        if (more) {
+          wait_landed(min(NS - 3, nk - 2 - t));
+          zero_k_tail(t + 1);
+        }
         barrier();
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(slot, 0);

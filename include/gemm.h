@@ -82,14 +82,16 @@ enum {
   GEMM_KERNEL_MFMA16_128x128_W1 = 20,  /* mfma16, 128x128 tile, K step 16, one wave */
   GEMM_KERNEL_MFMA_64x64_W1 = 21,      /* mfma32, 64x64 tile, K step 16, one wave */
   /* Kernels fed by direct global->LDS copies through a ring of LDS stages
-   * (K and N multiples of 4, 16-byte aligned A and B; other shapes run the
+   * (any K and N; shapes whose per-tile offsets would pass 2^31 bytes run the
    * register-staged kernel of the same tile). */
   GEMM_KERNEL_DMA32_256x256_W8 = 30,    /* mfma32, 256x256, K step 16, 8 waves, 4 stages */
-  GEMM_KERNEL_DMA32_256x256_W4 = 31,    /* mfma32, 256x256, K step 16, 4 waves, 4 stages */
   GEMM_KERNEL_DMA16_256x256_W8 = 32,    /* mfma16, 256x256, K step 16, 8 waves, 4 stages */
   GEMM_KERNEL_DMA32_128x128_W4 = 33,    /* mfma32, 128x128, K step 16, 4 waves, 4 stages */
   GEMM_KERNEL_DMA16_128x128_W4 = 34,    /* mfma16, 128x128, K step 16, 4 waves, 4 stages */
-  GEMM_KERNEL_DMA32_256x256_W8_S3 = 35  /* mfma32, 256x256, K step 16, 8 waves, 3 stages */
+  GEMM_KERNEL_DMA32_256x256_W8_S3 = 35, /* mfma32, 256x256, K step 16, 8 waves, 3 stages */
+  GEMM_KERNEL_DMA16_64x64 = 36,         /* mfma16, 64x64, K step 32, 4 waves, 4 stages */
+  GEMM_KERNEL_DMA32_64x64 = 37,         /* mfma32, 64x64, K step 16, 4 waves, 4 stages */
+  GEMM_KERNEL_DMA16_128x64 = 38         /* mfma16, 128x64, K step 32, 4 waves, 4 stages */
 };
 
 /* An execution plan: which kernel, and how many contiguous K ranges
