@@ -225,13 +225,15 @@ bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K
 }
 
 // Kernels fed by direct global -> LDS copies (16-byte copies from 4-byte
-// aligned sources, any K and N). Each lane's byte offset within a tile (at
-// most BM*K*4 for A, BK*N*4 for B) must stay below 2^31; returns false
-// (nothing launched) for shapes outside that.
+// aligned sources, any K and N). Each lane's byte offset from its tile's
+// first element (at most BM*K*4 for A, (k_chunk+BK)*N*4 for B) must stay
+// below 2^31; returns false (nothing launched) for shapes outside that.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE>
 bool launch_dma(const float *A, const float *B, float *out, int M, int N, int K,
                 const Resolved &r, long long slab, hipStream_t stream) {
-  if ((long long)BM * K * 4 >= (1LL << 31) || (long long)BK * N * 4 >= (1LL << 31)) return false;
+  if ((long long)BM * K * 4 >= (1LL << 31) ||
+      ((long long)r.k_chunk + BK) * N * 4 >= (1LL << 31))
+    return false;
   const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
   hipLaunchKernelGGL((gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE>),
                      grid, dim3(64 * WAVES_M * WAVES_N), 0, stream, A, B, out, M, N, K,

@@ -487,10 +487,15 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   using Op = Mfma<MI>;
   using acc_t = typename Op::acc_t;
   constexpr int FM = S::FM, FN = S::FN, KS = S::KS, NG = S::NG, NQ = S::NQ;
-  constexpr int CA = S::CA, EPA = S::EPA, RPA = S::RPA, IA = S::IA, EPB = S::EPB, RPB = S::RPB;
-  constexpr int LPW = S::LPW, NW = S::NWAVES;
+  constexpr int CA = S::CA, EPA = S::EPA, RPA = S::RPA, IA = S::IA, IB = S::IB;
+  constexpr int EPB = S::EPB, RPB = S::RPB, NW = S::NWAVES;
+  constexpr int LA = IA / NW, LB = IB / NW, LPW = LA + LB;   // copies per wave per step
+  constexpr int STAGE_F = S::STAGE_BYTES / 4;
+  static_assert(IA % NW == 0 && IB % NW == 0, "every wave copies the same number of A and B chunks");
+  static_assert(NG % 2 == 0 || NS % 2 == 0, "fragment slots repeat with the stage ring");
+  (void)FM; (void)FN;
 
-  __shared__ __attribute__((aligned(16))) float smem[NS * S::STAGE_BYTES / 4];
+  __shared__ __attribute__((aligned(16))) float smem[NS * STAGE_F];
   // One real store into the shared array, so the compiler cannot treat it as
   // never written (the copies write it behind the compiler's back).
   if (threadIdx.x == 0) smem[0] = 0.0f;
@@ -512,55 +517,70 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       static_cast<unsigned>(reinterpret_cast<unsigned long long>(
           (__attribute__((address_space(3))) float *)smem));
 
-  // Copy instructions of this wave: n = wave + NW * i over the IA A copies
-  // then the IB B copies of a stage. Per instruction, this lane's byte
-  // offset from the K step's base and its validity apart from the K range.
-  unsigned cp_off[LPW];
-  unsigned cp_lds[LPW];
-  int cp_k[LPW];       // A: the lane's first k within the step; B: its k row
-  bool cp_ok[LPW];     // row (A) or column (B) inside the matrix
-  bool cp_is_a[LPW];
+  // Copies of this wave, A copy i = workgroup copy wave + NW*i of the IA A
+  // copies of a stage, likewise for B. Per copy and lane: byte offset from the
+  // K step's base (already replaced by kOutOfRange when the row of A or the
+  // column of B lies outside the matrix), the k it covers, and the copy's
+  // byte offset within a stage (uniform).
+  unsigned a_voff[LA], a_lds[LA];
+  int a_k[LA];
+  bool a_ok[LA];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
+  for (int i = 0; i < LA; ++i) {
     const int n = wave + NW * i;
-    if (n < IA) {
-      // lane -> row r, physical float pe of that row; logical float ke
-      const int r = n * RPA + lane / EPA;
-      const int pe = (lane % EPA) * VEC;
-      const int ke = ((pe / 4) ^ swz_a<CA>(r)) * 4 + pe % 4;
-      cp_is_a[i] = true;
-      cp_ok[i] = m0 + r < M;
-      cp_k[i] = ke;
-      cp_off[i] = (static_cast<unsigned>(r) * static_cast<unsigned>(K) + ke) * 4u;
-      cp_lds[i] = static_cast<unsigned>(n * S::COPY_BYTES);
-    } else {
-      const int nb = n - IA;
-      const int k = nb * RPB + lane / EPB;
-      const int pe = (lane % EPB) * VEC;
-      const int ne = pe ^ (((k / KS) % NQ) * MI);
-      cp_is_a[i] = false;
-      cp_ok[i] = n0 + ne < N;
-      cp_k[i] = k;
-      cp_off[i] = (static_cast<unsigned>(k) * static_cast<unsigned>(N) + ne) * 4u;
-      cp_lds[i] = static_cast<unsigned>(S::A_BYTES + nb * S::COPY_BYTES);
-    }
+    const int r = n * RPA + lane / EPA;             // row within the tile
+    const int pe = (lane % EPA) * VEC;              // physical float within the row
+    const int ke = ((pe / 4) ^ swz_a<CA>(r)) * 4 + pe % 4;   // logical k within the step
+    a_ok[i] = m0 + r < M;
+    a_k[i] = ke;
+    a_voff[i] = a_ok[i] ? (static_cast<unsigned>(r) * static_cast<unsigned>(K) + ke) * 4u
+                        : kOutOfRange;
+    a_lds[i] = static_cast<unsigned>(n * S::COPY_BYTES);
   }
-  // Issue the copies of K step `step` into its stage.
-  // The ranges end exactly at the end of A and of B, so a chunk that runs
-  // past the last element of the matrix reads zeros there instead of memory
-  // beyond the allocation.
-  const long long a_elems = (long long)M * K, b_elems = (long long)K * N;
-  auto issue = [&](int step) {
-    const int k0 = k_begin + step * BK;
-    const long long a_first = (long long)m0 * K + k0, b_first = (long long)k0 * N + n0;
-    const u32x4 ra = make_buffer_rsrc(A + a_first, 4 * (a_elems - a_first));
-    const u32x4 rb = make_buffer_rsrc(B + b_first, 4 * (b_elems - b_first));
-    const unsigned stage = smem_base + static_cast<unsigned>((step % NS) * S::STAGE_BYTES);
+  unsigned b_voff[LB], b_lds[LB];
+  int b_k[LB];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const bool ok = cp_ok[i] && (k0 + cp_k[i] < k_end);
-      dma_copy<VEC>(cp_is_a[i] ? ra : rb, ok ? cp_off[i] : kOutOfRange, stage + cp_lds[i]);
-    }
+  for (int i = 0; i < LB; ++i) {
+    const int n = wave + NW * i;
+    const int k = n * RPB + lane / EPB;             // row of B within the step
+    const int pe = (lane % EPB) * VEC;
+    const int ne = pe ^ (((k / KS) % NQ) * MI);     // logical column within the tile
+    b_k[i] = k;
+    b_voff[i] = (n0 + ne < N) ? (static_cast<unsigned>(k) * static_cast<unsigned>(N) + ne) * 4u
+                              : kOutOfRange;
+    b_lds[i] = static_cast<unsigned>(S::A_BYTES + n * S::COPY_BYTES);
+  }
+
+  // One buffer resource per operand for the whole K range: base at the
+  // tile's first element, range ending exactly at the end of A (B), so a
+  // chunk running past the last element of a matrix reads zeros there. Step
+  // s adds s*BK floats (A) or s*BK rows (B) to each lane's offset; the host
+  // keeps every valid offset below 2^31 (BM*K*4 and k_chunk*N*4 bytes), and
+  // offsets that start at kOutOfRange stay past the range.
+  const long long a_first = (long long)m0 * K + k_begin, b_first = (long long)k_begin * N + n0;
+  const u32x4 ra = make_buffer_rsrc(A + a_first, 4 * ((long long)M * K - a_first));
+  const u32x4 rb = make_buffer_rsrc(B + b_first, 4 * ((long long)K * N - b_first));
+  const unsigned a_step_bytes = 4u * BK;
+  const unsigned b_step_bytes = 4u * BK * static_cast<unsigned>(N);
+  // Copies of a step whose K range is whole (every step but the last).
+  auto issue_full = [&](int step, unsigned stage_byte) {
+    const unsigned da = a_step_bytes * step, db = b_step_bytes * step;
+#pragma unroll
+    for (int i = 0; i < LA; ++i) dma_copy<VEC>(ra, a_voff[i] + da, stage_byte + a_lds[i]);
+#pragma unroll
+    for (int i = 0; i < LB; ++i) dma_copy<VEC>(rb, b_voff[i] + db, stage_byte + b_lds[i]);
+  };
+  // Copies of any step: chunks past the end of the K range read zeros.
+  auto issue_checked = [&](int step) {
+    const int kr = k_end - (k_begin + step * BK);   // K elements left in this step
+    const unsigned da = a_step_bytes * step, db = b_step_bytes * step;
+    const unsigned stage_byte = smem_base + static_cast<unsigned>((step % NS) * S::STAGE_BYTES);
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      dma_copy<VEC>(ra, a_k[i] < kr ? a_voff[i] + da : kOutOfRange, stage_byte + a_lds[i]);
+#pragma unroll
+    for (int i = 0; i < LB; ++i)
+      dma_copy<VEC>(rb, b_k[i] < kr ? b_voff[i] + db : kOutOfRange, stage_byte + b_lds[i]);
   };
   // Wait until this wave's copies of a step have landed while the copies of
   // `later` steps issued after it may stay in flight (vmcnt counts this
@@ -579,41 +599,43 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // have landed, it zeroes those floats in the chunks it copied itself.
   auto zero_k_tail = [&](int step) {
     if constexpr (VEC == 4) {
-      const int k0 = k_begin + step * BK;
-      if (step != nk - 1 || (k_end - k0) % 4 == 0) return;
-      const int stage_f = (step % NS) * (S::STAGE_BYTES / 4);
+      const int kr = k_end - (k_begin + step * BK);
+      if (step != nk - 1 || kr % 4 == 0) return;
+      float *stage = smem + (step % NS) * STAGE_F;
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int ks = k0 + cp_k[i];
-        if (cp_is_a[i] && cp_ok[i] && ks < k_end && ks + 4 > k_end) {
-          float *dst = smem + stage_f + cp_lds[i] / 4 + lane * 4;
-          for (int e = k_end - ks; e < 4; ++e) dst[e] = 0.0f;
+      for (int i = 0; i < LA; ++i) {
+        if (a_ok[i] && a_k[i] < kr && a_k[i] + 4 > kr) {
+          float *dst = stage + a_lds[i] / 4 + lane * 4;
+          for (int e = kr - a_k[i]; e < 4; ++e) dst[e] = 0.0f;
         }
       }
     }
   };
 
-  // Fragment reads (swizzled addresses), as in mfma_gemm_kernel.
+  // Fragment reads. Per lane the read offsets within a stage are fixed: for
+  // A row r = wm*WM + fm*MI + li the swizzle swz_a(r) does not depend on fm
+  // (fm*MI moves r by a multiple of 8 rows, or of 16 with CA = 8), and the
+  // B columns of lane group q are flipped by q*MI.
+  int a_rd[NG], b_rd[FN];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int r = wm * S::WM + li;
+    a_rd[g] = r * BK + 4 * (((q * KS + 4 * g) / 4) ^ swz_a<CA>(r));
+  }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+    b_rd[fn] = BM * BK + q * KS * BN + ((wn * S::WN + fn * MI + li) ^ (q * MI));
+
   floatx4 fa[2][FM];
   float fb[2][FN][4];
-  auto load_frags = [&](int step, int g, int slot) {
-    const float *st = smem + (step % NS) * (S::STAGE_BYTES / 4);
+  auto load_frags = [&](const float *st, int g, int slot) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int r = wm * S::WM + fm * MI + li;
-      const int lc = (q * KS + 4 * g) / 4;
-      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(st + r * BK + 4 * (lc ^ swz_a<CA>(r)));
-    }
+    for (int fm = 0; fm < FM; ++fm)
+      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(st + a_rd[g] + fm * MI * BK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = q * KS + 4 * g + j;
-      const int flip = ((k / KS) % NQ) * MI;   // column flip of row k, in floats
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int n = (wn * S::WN + fn * MI + li) ^ flip;
-        fb[slot][fn][j] = st[BM * BK + k * BN + n];
-      }
-    }
+      for (int fn = 0; fn < FN; ++fn) fb[slot][fn][j] = st[b_rd[fn] + (4 * g + j) * BN];
   };
 
   acc_t acc[FM][FN];
@@ -635,31 +657,68 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   barrier();  // the store into smem[0] precedes every copy
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue(s);
+    if (s < nk) issue_checked(s);
   wait_landed(min(NS - 2, nk - 1));
   zero_k_tail(0);
   barrier();
-  load_frags(0, 0, 0);
+  load_frags(smem, 0, 0);
 
-  auto k_step = [&](int t, auto parity) {
+  // Steady state: steps t whose copy target t+NS-1 is a whole, non-final
+  // step. The loop is unrolled over the ring, so stage offsets, fragment
+  // slots and wait counts are compile-time constants and no step needs a
+  // range check: the only branch is the loop's back edge.
+  auto k_step_main = [&](int t, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
+    const float *st = smem + ST * STAGE_F;
+    const float *st_next = smem + ((ST + 1) % NS) * STAGE_F;
+    constexpr unsigned issue_stage = static_cast<unsigned>(((ST + NS - 1) % NS) * S::STAGE_BYTES);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int slot = (ST * NG + g) & 1;
+      if (g < NG - 1) {
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(st, g + 1, slot ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        wait_vmcnt<(NS - 3) * LPW>();
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(st_next, 0, slot ^ 1);
+        issue_full(t + NS - 1, smem_base + issue_stage);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  // Any step, with the checks: the last NS or so steps.
+  auto k_step_tail = [&](int t, auto parity) {
     constexpr int P = decltype(parity)::value;
     const bool more = t + 1 < nk;
+    const float *st = smem + (t % NS) * STAGE_F;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int slot = (P * NG + g) & 1;
       if (g < NG - 1) {
         mfma_step(slot, 0);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(t, g + 1, slot ^ 1);
+        load_frags(st, g + 1, slot ^ 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // Steps up to t+NS-2 have been issued. Step t+1 has landed once every
-        // wave has waited for it (the later ones may stay in flight), and
-        // every read of step t-1's stage finished before the previous barrier,
-        // so after this barrier step t+NS-1 can be copied into that stage.
+        // wave has waited for it (later ones may stay in flight), and every
+        // read of step t-1's stage finished before the previous barrier, so
+        // after this barrier step t+NS-1 can be copied into that stage.
         if (more) {
           wait_landed(min(NS - 3, nk - 2 - t));
           zero_k_tail(t + 1);
@@ -668,8 +727,8 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(slot, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (more) load_frags(t + 1, 0, slot ^ 1);
-        if (t + NS - 1 < nk) issue(t + NS - 1);
+        if (more) load_frags(smem + ((t + 1) % NS) * STAGE_F, 0, slot ^ 1);
+        if (t + NS - 1 < nk) issue_checked(t + NS - 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
@@ -677,9 +736,19 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
     }
   };
-  for (int t = 0; t < nk; t += 2) {
-    k_step(t, std::integral_constant<int, 0>());
-    if (t + 1 < nk) k_step(t + 1, std::integral_constant<int, 1>());
+
+  const int n_main = nk > NS ? (nk - NS) / NS : 0;
+  int t = 0;
+  for (int it = 0; it < n_main; ++it, t += NS) {
+    k_step_main(t, std::integral_constant<int, 0>());
+    k_step_main(t + 1, std::integral_constant<int, 1>());
+    k_step_main(t + 2, std::integral_constant<int, 2>());
+    if constexpr (NS >= 4) k_step_main(t + 3, std::integral_constant<int, 3>());
+  }
+  // t is a multiple of NS here, hence even when NG is odd (NS is then even).
+  for (; t < nk; t += 2) {
+    k_step_tail(t, std::integral_constant<int, 0>());
+    if (t + 1 < nk) k_step_tail(t + 1, std::integral_constant<int, 1>());
   }
 
 #pragma unroll
