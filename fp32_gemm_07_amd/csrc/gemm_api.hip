@@ -8,6 +8,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <cmath>
 #include <mutex>
 
 #include "gemm_kernels.hpp"
@@ -94,42 +95,72 @@ size_t workspace_for(int M, int N, const Resolved &r) {
   return r.splits > 1 ? sizeof(float) * (size_t)r.splits * (size_t)M * (size_t)N : 0;
 }
 
-// The planner. Rules of thumb for one MI355X (256 CUs), from measured sweeps:
-//  - enough 256x256 tiles to give every CU one (>= 192): the 8-wave 256x256
-//    32x32x2 kernel fed by direct global->LDS copies, no split (137 TFLOP/s
-//    at 4096^3; shapes it cannot take run the register-staged kernel);
-//  - few output tiles but a long K: split K until about 256 workgroups,
-//    keeping each K range >= 1024 (256x256 tiles for wide outputs, 128x128
-//    for narrow ones);
-//  - otherwise 64x64 tiles of the 16x16x4 kernel (one workgroup per CU at
-//    1024x1024 outputs), copy-fed when K or N is not a multiple of 4.
-void plan(int M, int N, int K, int *kernel, int *split) {
-  *split = 1;
-  const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
-  const long long t128 = ceil_div(M, 128) * ceil_div(N, 128);
-  if (t256 >= 192) {
-    *kernel = GEMM_KERNEL_DMA32_256x256_W8;
-    return;
+// The planner: a cost model over three copy-fed kernels and power-of-two
+// K splits, fitted to timings of those kernels over square, wide, long-K and
+// ragged shapes on one MI355X. A CU works through its share of a launch's
+// workgroups (at most n = ceil(workgroups / CUs) of them), so a launch costs
+//   n * (2 * BM * BN * k_chunk / (rate_cu * eff) + per_wg) + fixed
+// with rate_cu = 256 FLOP/clk at 2.38 GHz and eff, per_wg (prologue and
+// epilogue of one workgroup) and fixed (launch, clock skew between XCDs)
+// per kernel below. Splitting K adds the partial sums (S slabs written and
+// read, C written), which stay in the last-level cache at these sizes,
+// at about 8 TB/s plus a fixed cost for the extra launch; and no launch is
+// cheaper than moving A, B and C once at about 5 TB/s. Workspace is capped
+// at 1 GiB.
+struct PlanCandidate {
+  int kernel;
+  double eff;
+  double per_wg_us;
+  double fixed_us;
+};
+constexpr PlanCandidate kPlanCandidates[] = {
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6},
+    {GEMM_KERNEL_DMA32_128x128_W4, 0.955, 4.8, 5.1},
+    {GEMM_KERNEL_DMA32_64x64, 0.91, 1.2, 6.5},
+};
+constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
+constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
+constexpr double kReduceFixedUs = 6.0;
+constexpr double kMaxWorkspaceBytes = 1024.0 * 1024.0 * 1024.0;
+constexpr double kHbmBytesPerUs = 5.0e6;
+
+double plan_cost_us(int M, int N, int K, const PlanCandidate &c, int split, int *splits_out) {
+  Resolved r;
+  if (!resolve(M, N, K, c.kernel, split, &r)) return 1e30;
+  const double wg = static_cast<double>(r.tiles_m * r.tiles_n * r.splits);
+  const double per_cu = std::ceil(wg / kNumCus);
+  const double flop = 2.0 * r.k->bm * r.k->bn * static_cast<double>(r.k_chunk);
+  double us = per_cu * (flop / (kRateCuFlopPerUs * c.eff) + c.per_wg_us) + c.fixed_us;
+  if (r.splits > 1) {
+    const double slab = 4.0 * M * static_cast<double>(N);
+    if (slab * r.splits > kMaxWorkspaceBytes) return 1e30;
+    us += (2.0 * r.splits + 1.0) * slab / kReduceBytesPerUs + kReduceFixedUs;
   }
-  const long long kmin = 1024;
-  if (K >= 4 * kmin) {
-    const bool wide = M >= 256 && N >= 256;
-    const long long tiles = wide ? t256 : t128;
-    long long s = std::max<long long>(1, kNumCus / std::max<long long>(1, tiles));
-    s = std::min<long long>(s, K / kmin);
-    if (s > 1 || tiles >= 96) {
-      *kernel = wide ? GEMM_KERNEL_DMA32_256x256_W8 : GEMM_KERNEL_DMA32_128x128_W4;
-      *split = static_cast<int>(s);
-      return;
+  // No launch beats reading A and B and writing C once (about 5 TB/s).
+  const double bytes = 4.0 * (static_cast<double>(M) * K + static_cast<double>(K) * N +
+                              static_cast<double>(M) * N);
+  *splits_out = r.splits;
+  return std::max(us, bytes / kHbmBytesPerUs + c.fixed_us);
+}
+
+void plan(int M, int N, int K, int *kernel, int *split) {
+  *kernel = kPlanCandidates[0].kernel;
+  *split = 1;
+  double best = 1e30;
+  for (const PlanCandidate &c : kPlanCandidates) {
+    for (int s = 1; s <= 64; s *= 2) {
+      if (s > 1 && K / s < 256) break;   // each K range keeps >= 256 elements
+      int launched = 1;
+      const double us = plan_cost_us(M, N, K, c, s, &launched);
+      if (launched < s) break;           // fewer K steps than ranges asked for
+      // Ties (within 1%) go to the candidate seen first: bigger tiles, fewer splits.
+      if (us < best * 0.99) {
+        best = us;
+        *kernel = c.kernel;
+        *split = s;
+      }
     }
   }
-  if (t128 >= 192) {
-    *kernel = GEMM_KERNEL_MFMA_128x128;
-    return;
-  }
-  // Rows that are not a whole number of 16-byte chunks: the copy-fed kernel's
-  // 16-byte copies beat the register-staged kernel's 4-byte loads.
-  *kernel = (K % 4 != 0 || N % 4 != 0) ? GEMM_KERNEL_DMA16_64x64 : GEMM_KERNEL_MFMA16_64x64;
 }
 
 // ---------------------------------------------------------------------------

@@ -464,7 +464,6 @@ struct DmaShape {
   static_assert(KS % 4 == 0 && (NG == 1 || NG % 2 == 0), "fragment groups");
   static_assert(NS >= 3 && NS <= 4, "3 or 4 stages");
   static_assert(NS * STAGE_BYTES <= 160 * 1024, "fits LDS");
-  static_assert((NS - 2) * LPW < 64, "vmcnt wait values fit the counter");
 };
 
 // Swizzle of A rows: with 4 chunks per row (BK = 16) 16 consecutive rows are
@@ -493,6 +492,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   constexpr int STAGE_F = S::STAGE_BYTES / 4;
   static_assert(IA % NW == 0 && IB % NW == 0, "every wave copies the same number of A and B chunks");
   static_assert(NG % 2 == 0 || NS % 2 == 0, "fragment slots repeat with the stage ring");
+  static_assert((NS - 1) * LPW < 64, "vmcnt wait values fit the counter");
   (void)FM; (void)FN;
 
   __shared__ __attribute__((aligned(16))) float smem[NS * STAGE_F];
@@ -587,8 +587,9 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // wave's outstanding copies, oldest first).
   auto wait_landed = [&](int later) {
     if constexpr (NS >= 4) {
-      if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
+      if (later >= 3) { wait_vmcnt<3 * LPW>(); return; }
     }
+    if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
     if (later >= 1) { wait_vmcnt<LPW>(); return; }
     wait_vmcnt<0>();
   };
@@ -653,25 +654,31 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
   };
 
-  // Prologue: steps 0 .. NS-2 in flight, step 0 landed, its first fragments.
+  // Schedule. One barrier per K step t, in its last fragment group. Every
+  // read of step t's stage was issued before it (the fragments of a step are
+  // read during the step before it and the step itself), so right after it
+  // that stage takes the copies of step t+NS; before it this wave waits until
+  // its copies of step t+1 (read from that group on) have landed, leaving
+  // steps t+2 .. t+NS-1 in flight.
+  //
+  // Prologue: all NS stages issued, step 0 landed, its first fragments.
   barrier();  // the store into smem[0] precedes every copy
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+  for (int s = 0; s < NS; ++s)
     if (s < nk) issue_checked(s);
-  wait_landed(min(NS - 2, nk - 1));
+  wait_landed(min(NS, nk) - min(1, nk));
   zero_k_tail(0);
   barrier();
   load_frags(smem, 0, 0);
 
-  // Steady state: steps t whose copy target t+NS-1 is a whole, non-final
-  // step. The loop is unrolled over the ring, so stage offsets, fragment
-  // slots and wait counts are compile-time constants and no step needs a
-  // range check: the only branch is the loop's back edge.
+  // Steady state: steps whose copy targets are whole, non-final steps. The
+  // loop is unrolled over the ring, so stage offsets, fragment slots and
+  // wait counts are compile-time constants and no step needs a range check:
+  // the only branch is the loop's back edge.
   auto k_step_main = [&](int t, auto stage_c) {
     constexpr int ST = decltype(stage_c)::value;
     const float *st = smem + ST * STAGE_F;
     const float *st_next = smem + ((ST + 1) % NS) * STAGE_F;
-    constexpr unsigned issue_stage = static_cast<unsigned>(((ST + NS - 1) % NS) * S::STAGE_BYTES);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int slot = (ST * NG + g) & 1;
@@ -684,13 +691,13 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        wait_vmcnt<(NS - 3) * LPW>();
+        wait_vmcnt<(NS - 2) * LPW>();
         barrier();
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(slot, 0);
         __builtin_amdgcn_sched_barrier(0);
         load_frags(st_next, 0, slot ^ 1);
-        issue_full(t + NS - 1, smem_base + issue_stage);
+        issue_full(t + NS, smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
@@ -698,7 +705,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
     }
   };
-  // Any step, with the checks: the last NS or so steps.
+  // Any step, with the checks: the last steps of the K range.
   auto k_step_tail = [&](int t, auto parity) {
     constexpr int P = decltype(parity)::value;
     const bool more = t + 1 < nk;
@@ -715,20 +722,18 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
         __builtin_amdgcn_sched_barrier(0);
       } else {
-        // Steps up to t+NS-2 have been issued. Step t+1 has landed once every
-        // wave has waited for it (later ones may stay in flight), and every
-        // read of step t-1's stage finished before the previous barrier, so
-        // after this barrier step t+NS-1 can be copied into that stage.
+        // Steps up to min(nk-1, t+NS-1) have been issued; step t+1 must
+        // have landed.
         if (more) {
-          wait_landed(min(NS - 3, nk - 2 - t));
+          wait_landed(min(nk - 1, t + NS - 1) - (t + 1));
           zero_k_tail(t + 1);
+          barrier();
         }
-        barrier();
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(slot, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (more) load_frags(smem + ((t + 1) % NS) * STAGE_F, 0, slot ^ 1);
-        if (t + NS - 1 < nk) issue_checked(t + NS - 1);
+        if (t + NS < nk) issue_checked(t + NS);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
@@ -737,7 +742,9 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     }
   };
 
-  const int n_main = nk > NS ? (nk - NS) / NS : 0;
+  // A main-loop pass covers steps t .. t+NS-1 and copies steps up to
+  // t+2*NS-1, which must all be whole and before the last step nk-1.
+  const int n_main = nk >= 2 * NS + 1 ? (nk - 2 * NS - 1) / NS + 1 : 0;
   int t = 0;
   for (int it = 0; it < n_main; ++it, t += NS) {
     k_step_main(t, std::integral_constant<int, 0>());

@@ -98,10 +98,18 @@ def test_invalid_plans_rejected():
 
 def test_planner_choices_for_standing_workloads():
     p4 = binding.gemm_f32_plan(4096, 4096, 4096)
-    assert p4.kernel == binding.GEMM_KERNEL_DMA32_256x256_W8 and p4.split_k == 1
+    assert p4.kernel == binding.GEMM_KERNEL_DMA32_256x256_W8_S3 and p4.split_k == 1
     p5 = binding.gemm_f32_plan(512, 512, 131072)
     assert p5.split_k > 1 and p5.k_chunk * p5.split_k >= 131072
     assert p5.k_chunk % 16 == 0
+    # few output tiles and a long K: small tiles, K split
+    p = binding.gemm_f32_plan(1024, 1024, 4096)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64
+    p = binding.gemm_f32_plan(256, 256, 8192)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64 and p.split_k > 1
+    # 24 x 24 tiles of 256 would leave a third round 25% full: 128x128 tiles
+    p = binding.gemm_f32_plan(6144, 6144, 6144)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_128x128_W4 and p.split_k == 1
     for (M, N, K) in [(128, 112, 96), (1024, 1024, 512), (1001, 777, 513), (1, 1, 1)]:
         p = binding.gemm_f32_plan(M, N, K)
         assert p.split_k >= 1 and p.k_chunk * p.split_k >= K
