@@ -39,7 +39,12 @@ DEFAULT_WORKLOAD = "square_4096"
 # (bench.py --copy-probe-mib 256): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
+        "fetch_kib": 196734.0, "write_kib": 65536.0,
+        "kernel_source_sha256": "9661b26330233a10eb1191fd7a59db46ff1264a63bf3f9d8eadf39281c39a4f3",
+    },
+}
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
 
 
@@ -61,9 +66,10 @@ def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    # The chip ramps its clock over the first ~20 ms of sustained MFMA load;
-    # 30 untimed steps (~30 ms at 4096^3) put the timed steps at steady state.
-    p.add_argument("--warmup", type=int, default=30)
+    # The chip ramps its clock over the first ~30 ms of sustained MFMA load
+    # (per-dispatch kernel traces: 1.1-1.2 ms at first, steady after ~30
+    # dispatches at 4096^3); 50 untimed steps put the timed ones past it.
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in gemm_inputs.WORKLOADS])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle's CPU-baseline sample")

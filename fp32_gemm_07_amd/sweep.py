@@ -1,0 +1,84 @@
+"""Time every copy-fed and register-staged plan over a list of shapes.
+
+    python -m fp32_gemm_07_amd.sweep [MxKxN ...]
+
+For each shape: the planner's choice, torch.matmul in FP32 (the vendor
+library, for context), and the four fastest (kernel, split) plans, each the
+median of HIP-event timings of back-to-back launches on inputs resident on
+the GPU (uniform [-1, 1) values; timing only, nothing is checked). This is
+the measurement the planner's cost model is fitted to.
+"""
+from __future__ import annotations
+
+import sys
+
+from . import binding, roofline
+
+DEFAULT_SHAPES = [
+    "128x96x112", "512x512x512", "1024x512x1024", "1001x513x777", "1024x1024x1024",
+    "2048x2048x2048", "1024x4096x1024", "2048x512x2048", "3000x3000x3000", "4096x1024x4096",
+    "8192x1024x8192", "256x8192x256", "512x131072x512", "4096x4096x4096", "6144x6144x6144",
+    "8192x8192x8192",
+]
+KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4", "dma16_128x128_w4",
+           "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64", "mfma32_128x128",
+           "mfma32_64x64", "valu_64x64"]
+SPLITS = (1, 2, 4, 8, 16, 32, 64)
+MAX_WORKSPACE = 2 << 30
+
+
+def main(argv=None) -> int:
+    import numpy as np
+    import torch
+    shapes = [tuple(int(x) for x in s.split("x")) for s in (argv or DEFAULT_SHAPES)]
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for (M, K, N) in shapes:
+        dA = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
+        dB = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+        dC = torch.empty((M, N), device="cuda")
+        flop = roofline.gemm_flops(M, N, K)
+        reps = max(5, min(200, int(0.15 / max(flop / 120e12, 1e-6))))
+
+        def timeit(call):
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                call()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+        def plan_call(plan):
+            need = binding.gemm_f32_plan_workspace_bytes(M, N, K, plan)
+            ws = torch.empty(max(need // 4, 1), device="cuda")
+            return lambda: binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, ws, need,
+                                                      stream.cuda_stream)
+
+        res = []
+        for kn in KERNELS:
+            for sp in SPLITS:
+                if sp > 1 and K // sp < 256:
+                    continue
+                plan = binding.make_plan(binding.KERNELS[kn], sp)
+                if binding.gemm_f32_plan_workspace_bytes(M, N, K, plan) > MAX_WORKSPACE:
+                    continue
+                res.append((timeit(plan_call(plan)), f"{kn}/S{sp}"))
+        auto = binding.gemm_f32_plan(M, N, K)
+        t_auto = timeit(plan_call(auto))
+        torch.backends.cuda.matmul.allow_tf32 = False
+        t_vendor = timeit(lambda: torch.matmul(dA, dB, out=dC))
+        res.sort()
+        top = "  ".join(f"{name} {us:.1f}" for us, name in res[:4])
+        print(f"{M}x{K}x{N}: auto {binding.gemm_kernel_name(auto.kernel)}/S{auto.split_k} "
+              f"{t_auto:.1f} us ({flop / t_auto / 1e6:.1f} TF) | vendor {t_vendor:.1f} us "
+              f"({flop / t_vendor / 1e6:.1f} TF) | best {top}", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
