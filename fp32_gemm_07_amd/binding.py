@@ -50,6 +50,10 @@ GEMM_KERNEL_DMA32_256x256_W8_S3 = 35
 GEMM_KERNEL_DMA16_64x64 = 36
 GEMM_KERNEL_DMA32_64x64 = 37
 GEMM_KERNEL_DMA16_128x64 = 38
+GEMM_KERNEL_LADDER_V0 = 40
+GEMM_KERNEL_LADDER_V1 = 41
+GEMM_KERNEL_LADDER_V2 = 42
+GEMM_KERNEL_LADDER_V3 = 43
 
 KERNELS = {
     "mfma32_256x256": GEMM_KERNEL_MFMA_256x256,
@@ -77,6 +81,10 @@ KERNELS = {
     "dma32_64x64": GEMM_KERNEL_DMA32_64x64,
     "dma16_128x64": GEMM_KERNEL_DMA16_128x64,
     "valu_64x64": GEMM_KERNEL_VALU_64x64,
+    "ladder_v0": GEMM_KERNEL_LADDER_V0,
+    "ladder_v1": GEMM_KERNEL_LADDER_V1,
+    "ladder_v2": GEMM_KERNEL_LADDER_V2,
+    "ladder_v3": GEMM_KERNEL_LADDER_V3,
 }
 
 # Every symbol include/gemm.h declares.

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libgemm.so")
 SOURCES = [os.path.join(CSRC, "gemm_api.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "gemm_kernels.hpp"), os.path.join(INCLUDE, "gemm.h")]
+DEPENDS = SOURCES + [os.path.join(CSRC, "gemm_kernels.hpp"), os.path.join(CSRC, "ladder_kernels.hpp"),
+                     os.path.join(INCLUDE, "gemm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIPCC_FLAGS = [

@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "gemm_kernels.hpp"
+#include "ladder_kernels.hpp"
 
 namespace {
 
@@ -58,6 +59,10 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_DMA16_64x64, 64, 64, 32, "dma_mfma16_f32_64x64x32_w4_s4"},
     {GEMM_KERNEL_DMA32_64x64, 64, 64, 16, "dma_mfma32_f32_64x64x16_w4_s4"},
     {GEMM_KERNEL_DMA16_128x64, 128, 64, 32, "dma_mfma16_f32_128x64x32_w4_s4"},
+    {GEMM_KERNEL_LADDER_V0, 16, 16, 16, "ladder_v0_naive_rows_along_lanes"},
+    {GEMM_KERNEL_LADDER_V1, 16, 16, 16, "ladder_v1_naive_cols_along_lanes"},
+    {GEMM_KERNEL_LADDER_V2, 16, 16, 16, "ladder_v2_lds_16x16x16"},
+    {GEMM_KERNEL_LADDER_V3, 16, 64, 16, "ladder_v3_lds_16x64x16_tn4"},
 };
 
 const KernelInfo *find_kernel(int id) {
@@ -369,6 +374,19 @@ void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N
       else
         hipLaunchKernelGGL(gemm::valu_gemm_kernel<true>, grid, dim3(gemm::kThreads), 0, stream, A,
                            B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
+      return;
+    }
+    case GEMM_KERNEL_LADDER_V0:
+    case GEMM_KERNEL_LADDER_V1:
+    case GEMM_KERNEL_LADDER_V2:
+    case GEMM_KERNEL_LADDER_V3: {
+      const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
+      auto *kern = r.k->id == GEMM_KERNEL_LADDER_V0   ? gemm::ladder_naive_kernel<true>
+                   : r.k->id == GEMM_KERNEL_LADDER_V1 ? gemm::ladder_naive_kernel<false>
+                   : r.k->id == GEMM_KERNEL_LADDER_V2 ? gemm::ladder_lds_kernel
+                                                      : gemm::ladder_coarse_kernel;
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, A, B, out, M, N, K, r.k_chunk,
+                         (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
       return;
     }
   }

@@ -1,12 +1,17 @@
 """Time every copy-fed and register-staged plan over a list of shapes.
 
     python -m fp32_gemm_07_amd.sweep [MxKxN ...]
+    python -m fp32_gemm_07_amd.sweep --ladder
 
 For each shape: the planner's choice, torch.matmul in FP32 (the vendor
 library, for context), and the four fastest (kernel, split) plans, each the
 median of HIP-event timings of back-to-back launches on inputs resident on
 the GPU (uniform [-1, 1) values; timing only, nothing is checked). This is
 the measurement the planner's cost model is fitted to.
+
+--ladder times the optimisation ladder of the yekq.top LeetGPU walkthrough
+(v0 .. v4, then the matrix-core kernels) on its two shapes, 1024 x 512 x 1024
+and 1001 x 513 x 777, with the mean of 50 launches as in its tables.
 """
 from __future__ import annotations
 
@@ -27,9 +32,65 @@ SPLITS = (1, 2, 4, 8, 16, 32, 64)
 MAX_WORKSPACE = 2 << 30
 
 
+LADDER_SHAPES = ["1024x512x1024", "1001x513x777"]
+# The walkthrough's rungs v0..v4, then the matrix-core kernels.
+LADDER = [("v0 naive, lanes along rows", "ladder_v0"), ("v1 naive, lanes along columns", "ladder_v1"),
+          ("v2 LDS tiles 16x16", "ladder_v2"), ("v3 LDS, 4 outputs per lane", "ladder_v3"),
+          ("v4 LDS, 4x4 outputs per lane", "valu_64x64"),
+          ("MFMA 32x32x2, register-staged 64x64", "mfma32_64x64"),
+          ("MFMA 32x32x2, copy-fed 64x64", "dma32_64x64")]
+
+
+def ladder(np, torch) -> int:
+    """Each rung of the ladder on the pages' two shapes, as in their tables."""
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    # ~0.1 s of matrix-core load first: the clock ramps up over the first
+    # tens of milliseconds of sustained load.
+    x = torch.rand((2048, 2048), device="cuda", generator=gen)
+    for _ in range(100):
+        torch.matmul(x, x)
+    torch.cuda.synchronize()
+    for shape in LADDER_SHAPES:
+        M, K, N = (int(x) for x in shape.split("x"))
+        dA = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
+        dB = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+        dC = torch.empty((M, N), device="cuda")
+        flop = roofline.gemm_flops(M, N, K)
+
+        def timeit(call, reps=50):
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                call()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+        torch.backends.cuda.matmul.allow_tf32 = False
+        t_vendor = timeit(lambda: torch.matmul(dA, dB, out=dC))
+        print(f"{shape} (M x K x N): mean of 50 launches after 3 warm-ups", flush=True)
+        print(f"  {'rung':40s} {'kernel':36s} {'us':>9s} {'GFLOP/s':>10s} {'vs vendor':>9s}")
+        for label, kn in LADDER:
+            plan = binding.make_plan(binding.KERNELS[kn], 1)
+            us = timeit(lambda: binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, None, 0,
+                                                           stream.cuda_stream))
+            print(f"  {label:40s} {binding.gemm_kernel_name(plan.kernel):36s} {us:9.2f} "
+                  f"{flop / us / 1e3:10.1f} {t_vendor / us:9.1%}", flush=True)
+        print(f"  {'torch.matmul FP32 (vendor library)':40s} {'':36s} {t_vendor:9.2f} "
+              f"{flop / t_vendor / 1e3:10.1f} {1:9.1%}", flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     import numpy as np
     import torch
+    if argv and argv[0] == "--ladder":
+        return ladder(np, torch)
     shapes = [tuple(int(x) for x in s.split("x")) for s in (argv or DEFAULT_SHAPES)]
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device="cuda").manual_seed(0)

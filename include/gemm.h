@@ -91,7 +91,13 @@ enum {
   GEMM_KERNEL_DMA32_256x256_W8_S3 = 35, /* mfma32, 256x256, K step 16, 8 waves, 3 stages */
   GEMM_KERNEL_DMA16_64x64 = 36,         /* mfma16, 64x64, K step 32, 4 waves, 4 stages */
   GEMM_KERNEL_DMA32_64x64 = 37,         /* mfma32, 64x64, K step 16, 4 waves, 4 stages */
-  GEMM_KERNEL_DMA16_128x64 = 38         /* mfma16, 128x64, K step 32, 4 waves, 4 stages */
+  GEMM_KERNEL_DMA16_128x64 = 38,        /* mfma16, 128x64, K step 32, 4 waves, 4 stages */
+  /* The optimisation ladder of the yekq.top LeetGPU walkthrough (sections v0
+   * to v3; its v4 is GEMM_KERNEL_VALU_64x64), for comparison only. */
+  GEMM_KERNEL_LADDER_V0 = 40,  /* one output per lane, lanes along rows (uncoalesced), 16x16 */
+  GEMM_KERNEL_LADDER_V1 = 41,  /* one output per lane, lanes along columns, 16x16 */
+  GEMM_KERNEL_LADDER_V2 = 42,  /* 16x16 LDS tiles, two barriers per 16-wide K phase */
+  GEMM_KERNEL_LADDER_V3 = 43   /* 16x64 tile, 4 outputs per lane along N, LDS K phases of 16 */
 };
 
 /* An execution plan: which kernel, and how many contiguous K ranges
