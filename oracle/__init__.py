@@ -55,6 +55,10 @@ class OracleLib:
         lib.oracle_gemm_f32_entries.restype = ctypes.c_int
         lib.oracle_gemm_f32_entries.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64,
                                                 vp, vp, ctypes.c_int]
+        lib.oracle_gemm_f32_general.restype = ctypes.c_int
+        lib.oracle_gemm_f32_general.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                                ctypes.c_float, vp, i64, vp, i64,
+                                                ctypes.c_float, vp, i64, vp, ctypes.c_int]
         lib.oracle_gemm_i64.restype = ctypes.c_int
         lib.oracle_gemm_i64.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int]
         self.lib = lib
@@ -92,6 +96,25 @@ class OracleLib:
                                               rows.size, _ptr(out), _ptr(S), threads)
         if rc != 0:
             raise RuntimeError(f"oracle_gemm_f32_entries failed: {rc}")
+        return out, S
+
+    def gemm_general(self, trans_a: bool, trans_b: bool, M: int, N: int, K: int, alpha: float,
+                     A: np.ndarray, lda: int, B: np.ndarray, ldb: int, beta: float,
+                     C: np.ndarray, ldc: int, threads: int = 0):
+        """C <- alpha * op(A) op(B) + beta * C on strided row-major storage.
+
+        A, B and C are the flat float32 storage arrays (padding included); the
+        result is a new flat array (C's storage with the M x N elements
+        replaced) and S (float64 M x N)."""
+        A = np.ascontiguousarray(A, dtype=np.float32).ravel()
+        B = np.ascontiguousarray(B, dtype=np.float32).ravel()
+        out = np.array(C, dtype=np.float32).ravel()
+        S = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_gemm_f32_general(int(bool(trans_a)), int(bool(trans_b)), M, N, K,
+                                              alpha, _ptr(A), lda, _ptr(B), ldb, beta, _ptr(out),
+                                              ldc, _ptr(S), threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_f32_general failed: {rc}")
         return out, S
 
     def gemm_i64(self, A: np.ndarray, B: np.ndarray, threads: int = 0) -> np.ndarray:
@@ -144,6 +167,12 @@ def gemm_i64(A: np.ndarray, B: np.ndarray, threads: int = 0) -> np.ndarray:
     return _lib().gemm_i64(A, B, threads)
 
 
+def gemm_general(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, threads=0):
+    return _lib().gemm_general(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                               threads)
+
+
 gemm.__doc__ = OracleLib.gemm.__doc__
 gemm_entries.__doc__ = OracleLib.gemm_entries.__doc__
 gemm_i64.__doc__ = OracleLib.gemm_i64.__doc__
+gemm_general.__doc__ = OracleLib.gemm_general.__doc__

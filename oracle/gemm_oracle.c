@@ -125,6 +125,72 @@ int oracle_gemm_f32_entries(const float *A, const float *B, int64_t M,
 }
 
 /*
+ * General form, in the shape of the BLAS SGEMM call that the LeetGPU
+ * walkthrough's cuBLAS reference section makes, for row-major storage:
+ *
+ *   C[i][j] <- alpha * sum_{k=0}^{K-1} opA(i, k) * opB(k, j) + beta * C[i][j]
+ *
+ *   opA(i, k) = A[i*lda + k]           (trans_a == 0: A stored M x K)
+ *             = A[k*lda + i]           (trans_a != 0: A stored K x M, i.e. A^T)
+ *   opB(k, j) = B[k*ldb + j]           (trans_b == 0: B stored K x N)
+ *             = B[j*ldb + k]           (trans_b != 0: B stored N x K)
+ *   element (i, j) of C at C[i*ldc + j].
+ *
+ * The pages fix alpha = 1, beta = 0 and dense storage (the plain function
+ * above); the general form takes the BLAS conventions, read as:
+ *   - the sum is the plain function's: FP64, ascending k, from +0.0;
+ *   - alpha * sum + beta * c is formed in double (c the FP32 value held in C)
+ *     and rounded once to FP32;
+ *   - beta == 0: C is not read (NaN or garbage in C does not matter) and the
+ *     result is alpha * sum;
+ *   - alpha == 0 or K == 0: A and B are not read and the result is beta * c,
+ *     or +0.0 when beta == 0;
+ *   - only the M x N elements are written; the rest of each C row (up to
+ *     ldc) is left as it was.
+ * S (dense M x N, may be null) receives |alpha| * sum_k |opA * opB| + |beta * c|,
+ * the scale of the acceptance bound.
+ */
+int oracle_gemm_f32_general(int trans_a, int trans_b, int64_t M, int64_t N,
+                            int64_t K, float alpha, const float *A,
+                            int64_t lda, const float *B, int64_t ldb,
+                            float beta, float *C, int64_t ldc, double *S,
+                            int threads) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  if (M == 0 || N == 0) return 0;
+  const int use_ab = alpha != 0.0f && K > 0;
+  if (!C || ldc < N) return -1;
+  if (use_ab && (!A || !B)) return -1;
+  if (use_ab && lda < (trans_a ? M : K)) return -1;
+  if (use_ab && ldb < (trans_b ? K : N)) return -1;
+  if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel for num_threads(threads) schedule(static)
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      double sum = 0.0, sab = 0.0;
+      if (use_ab) {
+        for (int64_t k = 0; k < K; ++k) {
+          const double a = trans_a ? (double)A[k * lda + i] : (double)A[i * lda + k];
+          const double b = trans_b ? (double)B[j * ldb + k] : (double)B[k * ldb + j];
+          sum += a * b;
+          sab += fabs(a * b);
+        }
+      }
+      const double c = beta != 0.0f ? (double)C[i * ldc + j] : 0.0;
+      double r;
+      if (!use_ab)
+        r = beta != 0.0f ? (double)beta * c : 0.0;
+      else if (beta == 0.0f)
+        r = (double)alpha * sum;
+      else
+        r = (double)alpha * sum + (double)beta * c;
+      C[i * ldc + j] = (float)r;
+      if (S) S[i * N + j] = fabs((double)alpha) * sab + fabs((double)beta * c);
+    }
+  }
+  return 0;
+}
+
+/*
  * Exact integer product: C[i][j] = sum_k A[i][k] * B[k][j] in int64.
  * Exact as long as no partial sum leaves the int64 range; the callers keep
  * |A|, |B| <= 16 and K <= 2^17, far inside it.

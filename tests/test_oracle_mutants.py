@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+from test_oracle_general_pins import GENERAL, case_matches, run_case
 from test_oracle_pins import HAND, _python_int_gemm
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gemm_oracle.c")
@@ -34,6 +35,19 @@ MUTANTS = [
     ("entries_wrong_column", "(double)A[i * K + k] * (double)B[k * N + j];",
      "(double)A[i * K + k] * (double)B[k * N + i];"),
     ("i64_adds_instead_of_multiplies", "crow[j] += a * brow[j];", "crow[j] += a + brow[j];"),
+    # the general form
+    ("general_lda_taken_as_K", "(double)A[i * lda + k];", "(double)A[i * K + k];"),
+    ("general_transposed_a_indexed_as_plain", "(double)A[k * lda + i]", "(double)A[i * lda + k]"),
+    ("general_transposed_b_indexed_as_plain", "(double)B[j * ldb + k]", "(double)B[k * ldb + j]"),
+    ("general_ldc_taken_as_N", "C[i * ldc + j] = (float)r;", "C[i * N + j] = (float)r;"),
+    ("general_alpha_not_applied", "r = (double)alpha * sum + (double)beta * c;",
+     "r = sum + (double)beta * c;"),
+    ("general_beta_not_applied", "r = (double)alpha * sum + (double)beta * c;",
+     "r = (double)alpha * sum + c;"),
+    ("general_c_read_when_beta_zero", "const double c = beta != 0.0f ? (double)C[i * ldc + j] : 0.0;",
+     "const double c = (double)C[i * ldc + j];"),
+    ("general_ab_read_when_alpha_zero", "const int use_ab = alpha != 0.0f && K > 0;",
+     "const int use_ab = K > 0;"),
 ]
 
 
@@ -64,6 +78,11 @@ def _pin_failures(lib: "oracle.OracleLib"):
     C, _ = lib.gemm(np.zeros((3, 0), np.float32), np.zeros((0, 4), np.float32))
     if not np.all(C.view(np.uint32) == 0):
         failed.append("empty_sum")
+
+    for case in GENERAL:
+        out, S = run_case(lib, case)
+        if not case_matches(out, case["Cout"]) or not np.isfinite(S).all():
+            failed.append("general:" + case["name"])
 
     rng = np.random.default_rng(3)
     for (M, K, N) in [(3, 5, 2), (7, 4, 9)]:
