@@ -90,8 +90,9 @@ KERNELS = {
 # Every symbol include/gemm.h declares.
 EXPORTS = (
     "gemm_f32", "gemm_f32_workspace_bytes", "gemm_f32_ex", "gemm_f32_plan",
-    "gemm_f32_plan_workspace_bytes", "gemm_f32_with_plan", "gemm_kernel_name",
-    "gemm_status_string", "gemm_last_hip_error",
+    "gemm_f32_plan_workspace_bytes", "gemm_f32_with_plan", "gemm_f32_general",
+    "gemm_f32_general_workspace_bytes", "gemm_kernel_name", "gemm_status_string",
+    "gemm_last_hip_error",
 )
 
 
@@ -161,6 +162,11 @@ def load():
         lib.gemm_f32_plan_workspace_bytes.restype = sz
         lib.gemm_f32_with_plan.argtypes = [vp, vp, vp, i, i, i, plan_p, vp, sz, vp]
         lib.gemm_f32_with_plan.restype = i
+        f = ctypes.c_float
+        lib.gemm_f32_general.argtypes = [i, i, i, i, i, f, vp, i, vp, i, f, vp, i, vp, sz, vp]
+        lib.gemm_f32_general.restype = i
+        lib.gemm_f32_general_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        lib.gemm_f32_general_workspace_bytes.restype = sz
         lib.gemm_kernel_name.argtypes = [i]
         lib.gemm_kernel_name.restype = ctypes.c_char_p
         lib.gemm_status_string.argtypes = [i]
@@ -218,6 +224,21 @@ def gemm_f32_with_plan(A, B, C, M: int, N: int, K: int, plan: gemm_plan_t, works
     _check(load().gemm_f32_with_plan(_addr(A), _addr(B), _addr(C), M, N, K, ctypes.byref(plan),
                                      _addr(workspace) or None, workspace_bytes, stream or None),
            "gemm_f32_with_plan")
+
+
+def gemm_f32_general(trans_a: bool, trans_b: bool, M: int, N: int, K: int, alpha: float, A,
+                     lda: int, B, ldb: int, beta: float, C, ldc: int, workspace=None,
+                     workspace_bytes: int = 0, stream: int = 0) -> None:
+    _check(load().gemm_f32_general(int(bool(trans_a)), int(bool(trans_b)), M, N, K, alpha,
+                                   _addr(A) or None, lda, _addr(B) or None, ldb, beta,
+                                   _addr(C) or None, ldc, _addr(workspace) or None,
+                                   workspace_bytes, stream or None), "gemm_f32_general")
+
+
+def gemm_f32_general_workspace_bytes(trans_a: bool, trans_b: bool, M: int, N: int, K: int,
+                                     lda: int, ldb: int) -> int:
+    return int(load().gemm_f32_general_workspace_bytes(int(bool(trans_a)), int(bool(trans_b)),
+                                                       M, N, K, lda, ldb))
 
 
 def gemm_kernel_name(kernel: int) -> str:

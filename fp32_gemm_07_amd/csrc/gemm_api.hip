@@ -100,6 +100,43 @@ size_t workspace_for(int M, int N, const Resolved &r) {
   return r.splits > 1 ? sizeof(float) * (size_t)r.splits * (size_t)M * (size_t)N : 0;
 }
 
+// One product C <- alpha * op(A) op(B) + beta * C on strided row-major
+// storage (the plain entry points: no transposes, lda = K, ldb = N, ldc = N,
+// alpha = 1, beta = 0).
+struct Problem {
+  bool ta, tb;   // op(A) = A^T (A stored K x M), op(B) = B^T (B stored N x K)
+  int M, N, K;
+  float alpha, beta;
+  const float *A, *B;
+  float *C;
+  int lda, ldb, ldc;
+};
+
+Problem plain_problem(const float *A, const float *B, float *C, int M, int N, int K) {
+  return Problem{false, false, M, N, K, 1.0f, 0.0f, A, B, C, K, N, N};
+}
+
+// The copy-fed kernels address an operand tile with 32-bit byte offsets from
+// its first element: they must stay below 2^31 over the K range of one
+// workgroup. K-contiguous operand: about (BX*ld + k_span)*4 bytes;
+// M/N-contiguous: about (k_span*ld + BX)*4.
+constexpr long long kMaxOffset = 1LL << 31;
+bool operand_fits(bool kmajor, int bx, int ld, long long k_span) {
+  const long long bytes = kmajor ? 4 * ((long long)bx * ld + k_span)
+                                 : 4 * (k_span * ld + bx);
+  return bytes < kMaxOffset;
+}
+bool dma_fits(const Problem &p, int bm, int bn, int bk, int k_chunk) {
+  const long long span = (long long)k_chunk + bk;
+  return operand_fits(!p.ta, bm, p.lda, span) && operand_fits(p.tb, bn, p.ldb, span);
+}
+// The K-contiguous limit does not depend on K: whether a tile size can be
+// used at all for these row strides.
+bool dma_tile_usable(const Problem &p, int bm, int bn, int bk) {
+  return (p.ta || operand_fits(true, bm, p.lda, 2 * bk)) &&
+         (!p.tb || operand_fits(true, bn, p.ldb, 2 * bk));
+}
+
 // The planner: a cost model over three copy-fed kernels and power-of-two
 // K splits, fitted to timings of those kernels over square, wide, long-K and
 // ragged shapes on one MI355X. A CU works through its share of a launch's
@@ -148,11 +185,15 @@ double plan_cost_us(int M, int N, int K, const PlanCandidate &c, int split, int 
   return std::max(us, bytes / kHbmBytesPerUs + c.fixed_us);
 }
 
-void plan(int M, int N, int K, int *kernel, int *split) {
+void plan(int M, int N, int K, int *kernel, int *split, const Problem *general = nullptr) {
   *kernel = kPlanCandidates[0].kernel;
   *split = 1;
   double best = 1e30;
   for (const PlanCandidate &c : kPlanCandidates) {
+    if (general) {
+      const KernelInfo *k = find_kernel(c.kernel);
+      if (!dma_tile_usable(*general, k->bm, k->bn, k->bk)) continue;
+    }
     for (int s = 1; s <= 64; s *= 2) {
       if (s > 1 && K / s < 256) break;   // each K range keeps >= 256 elements
       int launched = 1;
@@ -261,110 +302,143 @@ bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K
 }
 
 // Kernels fed by direct global -> LDS copies (16-byte copies from 4-byte
-// aligned sources, any K and N). Each lane's byte offset from its tile's
-// first element (at most BM*K*4 for A, (k_chunk+BK)*N*4 for B) must stay
-// below 2^31; returns false (nothing launched) for shapes outside that.
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE>
-bool launch_dma(const float *A, const float *B, float *out, int M, int N, int K,
-                const Resolved &r, long long slab, hipStream_t stream) {
-  if ((long long)BM * K * 4 >= (1LL << 31) ||
-      ((long long)r.k_chunk + BK) * N * 4 >= (1LL << 31))
-    return false;
+// aligned sources, any K, N and row strides, either storage order of each
+// operand). Writes alpha * op(A) op(B) + beta * out (row stride ldo) for the
+// tile's K range. Returns false (nothing launched) when the operand offsets
+// of one workgroup would not fit in 32 bits.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE, bool A_KM,
+          bool B_KM>
+void launch_dma_t(const Problem &p, float *out, int ldo, float alpha, float beta,
+                  const Resolved &r, long long slab, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
-  hipLaunchKernelGGL((gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE>),
-                     grid, dim3(64 * WAVES_M * WAVES_N), 0, stream, A, B, out, M, N, K,
-                     r.k_chunk, static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n),
-                     r.splits, slab);
-  return true;
+  hipLaunchKernelGGL(
+      (gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE, A_KM, B_KM>), grid,
+      dim3(64 * WAVES_M * WAVES_N), 0, stream, p.A, p.B, out, p.M, p.N, p.K, p.lda, p.ldb, ldo,
+      alpha, beta, r.k_chunk, static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits,
+      slab);
 }
 
-// Launch the kernel of r.k (falling back to a configuration with 4-byte
-// loads where the chosen one has none for this shape).
-void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N, int K,
+// ALL_ORDERS: the configuration is built for transposed operands too (the
+// planner's three); the others take op(A) = A, op(B) = B only.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE,
+          bool ALL_ORDERS>
+bool launch_dma(const Problem &p, float *out, int ldo, float alpha, float beta,
+                const Resolved &r, long long slab, hipStream_t stream) {
+  if (!dma_fits(p, BM, BN, BK, r.k_chunk)) return false;
+#define LGEMM_DMA(AK, BKM)                                                                    \
+  launch_dma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, WPE, AK, BKM>(p, out, ldo, alpha, beta, r, \
+                                                                  slab, stream)
+  if (!p.ta && !p.tb) {
+    LGEMM_DMA(true, false);
+    return true;
+  }
+  if constexpr (ALL_ORDERS) {
+    if (p.ta && !p.tb) LGEMM_DMA(false, false);
+    else if (!p.ta && p.tb) LGEMM_DMA(true, true);
+    else LGEMM_DMA(false, true);
+    return true;
+  }
+#undef LGEMM_DMA
+  return false;
+}
+
+// Launch the kernel of r.k, writing alpha * op(A) op(B) + beta * out (row
+// stride ldo). Register-staged, vector-FMA and ladder kernels take the plain
+// problem only (op = identity, dense, ldo = N, alpha = 1, beta = 0); a
+// copy-fed kernel whose offsets would not fit runs the register-staged kernel
+// of its tile for a plain problem. Returns false if nothing could be launched.
+bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, float beta,
                         const Resolved &r, long long slab, hipStream_t stream) {
+  const float *A = p.A, *B = p.B;
+  const int M = p.M, N = p.N, K = p.K;
+  const bool plain = !p.ta && !p.tb && p.lda == K && p.ldb == N && ldo == N && alpha == 1.0f &&
+                     beta == 0.0f;
+  const bool dma_kernel = r.k->id >= GEMM_KERNEL_DMA32_256x256_W8 &&
+                          r.k->id <= GEMM_KERNEL_DMA16_128x64;
+  if (!plain && !dma_kernel) return false;
   switch (r.k->id) {
     case GEMM_KERNEL_MFMA_256x256:
       launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA_256x256_W8:
       if (!launch_mfma<32, 256, 256, 16, 2, 4, 2, false>(A, B, out, M, N, K, r, slab, stream))
         launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA_256x128:
       launch_mfma<32, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA_128x128:
       launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA_64x64:
       launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_256x256:
       launch_mfma<16, 256, 256, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_256x256_W8:
       if (!launch_mfma<16, 256, 256, 32, 2, 4, 2, false>(A, B, out, M, N, K, r, slab, stream))
         launch_mfma<16, 256, 256, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_256x128:
       launch_mfma<16, 256, 128, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_128x128:
       launch_mfma<16, 128, 128, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_64x64:
       launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_256x256_K16:
       launch_mfma<16, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_128x128_K16:
       launch_mfma<16, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_256x128_K16:
       launch_mfma<16, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA_128x128_W1:
       launch_mfma<32, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA16_128x128_W1:
       launch_mfma<16, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_MFMA_64x64_W1:
       launch_mfma<32, 64, 64, 16, 1, 1, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return true;
     case GEMM_KERNEL_DMA32_256x256_W8:
-      if (!launch_dma<32, 256, 256, 16, 2, 4, 4, 2>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<32, 256, 256, 16, 2, 4, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
+                                                             stream) ||
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
-      if (!launch_dma<32, 256, 256, 16, 2, 4, 3, 2>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, out, ldo, alpha, beta, r, slab,
+                                                            stream) ||
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA16_256x256_W8:
-      if (!launch_dma<16, 256, 256, 16, 2, 4, 4, 2>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<16, 256, 256, 16, 2, 4, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
+                                                             stream) ||
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA32_128x128_W4:
-      if (!launch_dma<32, 128, 128, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,
+                                                            stream) ||
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA16_128x128_W4:
-      if (!launch_dma<16, 128, 128, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<16, 128, 128, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
+                                                             stream) ||
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA16_64x64:
-      launch_dma<16, 64, 64, 32, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream) ||
-          launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<16, 64, 64, 32, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
+                                                           stream) ||
+             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA32_64x64:
-      launch_dma<32, 64, 64, 16, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream) ||
-          launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,
+                                                          stream) ||
+             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA16_128x64:
-      launch_dma<16, 128, 64, 32, 2, 2, 4, 2>(A, B, out, M, N, K, r, slab, stream) ||
-          launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
-      return;
+      return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
+                                                            stream) ||
+             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
@@ -374,7 +448,7 @@ void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N
       else
         hipLaunchKernelGGL(gemm::valu_gemm_kernel<true>, grid, dim3(gemm::kThreads), 0, stream, A,
                            B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
-      return;
+      return true;
     }
     case GEMM_KERNEL_LADDER_V0:
     case GEMM_KERNEL_LADDER_V1:
@@ -387,47 +461,83 @@ void launch_gemm_kernel(const float *A, const float *B, float *out, int M, int N
                                                       : gemm::ladder_coarse_kernel;
       hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, A, B, out, M, N, K, r.k_chunk,
                          (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
-      return;
+      return true;
     }
   }
+  return false;
 }
 
-int launch(const float *A, const float *B, float *C, int M, int N, int K, const Resolved &r,
-           void *workspace, hipStream_t stream) {
-  float *out = r.splits > 1 ? static_cast<float *>(workspace) : C;
-  const long long slab = r.splits > 1 ? (long long)M * N : 0;
-  launch_gemm_kernel(A, B, out, M, N, K, r, slab, stream);
+// One pass of the product with a resolved plan: the kernel, then (split K)
+// the reduction of the partial slabs into C with alpha and beta.
+int launch(const Problem &p, const Resolved &r, void *workspace, hipStream_t stream) {
+  const bool split = r.splits > 1;
+  float *out = split ? static_cast<float *>(workspace) : p.C;
+  const long long slab = split ? (long long)p.M * p.N : 0;
+  if (!launch_gemm_kernel(p, out, split ? p.N : p.ldc, split ? 1.0f : p.alpha,
+                          split ? 0.0f : p.beta, r, slab, stream))
+    return GEMM_ERR_INVALID_PLAN;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
-  if (r.splits > 1) {
-    const long long count = (long long)M * N;
-    const bool v4 = (count % 4 == 0) && (reinterpret_cast<uintptr_t>(C) % 16 == 0) &&
+  if (split) {
+    const long long count = (long long)p.M * p.N;
+    const bool v4 = (p.N % 4 == 0) && (p.ldc % 4 == 0) &&
+                    (reinterpret_cast<uintptr_t>(p.C) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(workspace) % 16 == 0);
     const long long items = v4 ? count / 4 : count;
     const unsigned blocks =
         static_cast<unsigned>(std::min<long long>(ceil_div(items, gemm::kThreads), 4 * kNumCus));
+    const float *ws = static_cast<const float *>(workspace);
     if (v4)
       hipLaunchKernelGGL(gemm::splitk_reduce_kernel<4>, dim3(blocks), dim3(gemm::kThreads), 0,
-                         stream, static_cast<const float *>(workspace), C, count, r.splits);
+                         stream, ws, p.C, count, p.N, p.ldc, r.splits, p.alpha, p.beta);
     else
       hipLaunchKernelGGL(gemm::splitk_reduce_kernel<1>, dim3(blocks), dim3(gemm::kThreads), 0,
-                         stream, static_cast<const float *>(workspace), C, count, r.splits);
+                         stream, ws, p.C, count, p.N, p.ldc, r.splits, p.alpha, p.beta);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
   }
   return GEMM_OK;
 }
 
-int launch_fill_zero(float *C, long long count, hipStream_t stream) {
+// C <- beta * C (+0.0 when beta == 0): the product when K = 0 or alpha = 0.
+int launch_scale_c(const Problem &p, hipStream_t stream) {
+  const long long count = (long long)p.M * p.N;
   const unsigned blocks =
       static_cast<unsigned>(std::min<long long>(ceil_div(count, gemm::kThreads), 4 * kNumCus));
-  hipLaunchKernelGGL(gemm::fill_zero_kernel, dim3(blocks), dim3(gemm::kThreads), 0, stream, C,
-                     count);
+  hipLaunchKernelGGL(gemm::scale_c_kernel, dim3(blocks), dim3(gemm::kThreads), 0, stream, p.C,
+                     count, p.N, p.ldc, p.beta);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? GEMM_OK : hip_fail(e);
 }
 
-// Common path for every entry point. `plan_in` null = planner. `own_ws`:
+// The library's per-device workspace, grown to `need` bytes if possible.
+// Returns it, or null if it could not be allocated.
+void *library_workspace(int dev, size_t need, int *status) {
+  *status = GEMM_OK;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_ws_bytes[dev] < need) {
+    if (g_ws[dev]) {
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) {
+        *status = hip_fail(e);
+        return nullptr;
+      }
+      (void)hipFree(g_ws[dev]);
+      g_ws[dev] = nullptr;
+      g_ws_bytes[dev] = 0;
+    }
+    void *q = nullptr;
+    if (hipMalloc(&q, need) == hipSuccess) {
+      g_ws[dev] = q;
+      g_ws_bytes[dev] = need;
+    } else {
+      (void)hipGetLastError();
+    }
+  }
+  return g_ws_bytes[dev] >= need ? g_ws[dev] : nullptr;
+}
+
+// Common path of the plain entry points. `plan_in` null = planner. `own_ws`:
 // use (and grow) the library's per-device workspace instead of the caller's.
 int run(const float *A, const float *B, float *C, int M, int N, int K, const gemm_plan_t *plan_in,
         void *workspace, size_t workspace_bytes, bool own_ws, hipStream_t stream) {
@@ -451,35 +561,115 @@ int run(const float *A, const float *B, float *C, int M, int N, int K, const gem
   int dev = 0;
   st = check_device(&dev);
   if (st != GEMM_OK) return st;
-  if (K == 0) return launch_fill_zero(C, (long long)M * N, stream);
+  const Problem p = plain_problem(A, B, C, M, N, K);
+  if (K == 0) return launch_scale_c(p, stream);
 
   if (own_ws && need > 0) {
-    std::lock_guard<std::mutex> lock(g_mu);
-    if (g_ws_bytes[dev] < need) {
-      if (g_ws[dev]) {
-        hipError_t e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e);
-        (void)hipFree(g_ws[dev]);
-        g_ws[dev] = nullptr;
-        g_ws_bytes[dev] = 0;
-      }
-      void *p = nullptr;
-      if (hipMalloc(&p, need) == hipSuccess) {
-        g_ws[dev] = p;
-        g_ws_bytes[dev] = need;
-      } else {
-        (void)hipGetLastError();
-      }
-    }
-    if (g_ws_bytes[dev] >= need) {
-      workspace = g_ws[dev];
-    } else {
-      // No workspace available: same kernel without the split.
-      if (!resolve(M, N, K, kernel, 1, &r)) return GEMM_ERR_INVALID_PLAN;
-      workspace = nullptr;
-    }
+    workspace = library_workspace(dev, need, &st);
+    if (st != GEMM_OK) return st;
+    // No workspace available: same kernel without the split.
+    if (!workspace && !resolve(M, N, K, kernel, 1, &r)) return GEMM_ERR_INVALID_PLAN;
   }
-  return launch(A, B, C, M, N, K, r, workspace, stream);
+  return launch(p, r, workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The general form: transposes, row strides, alpha and beta.
+int validate_general(const Problem &p) {
+  if (p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_DIM;
+  const int a_cols = p.ta ? p.M : p.K, b_cols = p.tb ? p.K : p.N;
+  if (p.lda < std::max(1, a_cols) || p.ldb < std::max(1, b_cols) || p.ldc < std::max(1, p.N))
+    return GEMM_ERR_INVALID_DIM;
+  const long long a_rows = p.ta ? p.K : p.M, b_rows = p.tb ? p.N : p.K;
+  if (a_rows * p.lda > (1LL << 40) || b_rows * p.ldb > (1LL << 40) ||
+      (long long)p.M * p.ldc > (1LL << 40))
+    return GEMM_ERR_INVALID_DIM;
+  const bool any_out = p.M > 0 && p.N > 0;
+  const bool uses_ab = any_out && p.K > 0 && p.alpha != 0.0f;
+  // Byte extents from each operand's first to its last element.
+  const size_t a_bytes = uses_ab ? sizeof(float) * (size_t)((a_rows - 1) * p.lda + a_cols) : 0;
+  const size_t b_bytes = uses_ab ? sizeof(float) * (size_t)((b_rows - 1) * p.ldb + b_cols) : 0;
+  const size_t c_bytes = any_out ? sizeof(float) * (size_t)((long long)(p.M - 1) * p.ldc + p.N) : 0;
+  if ((a_bytes && !p.A) || (b_bytes && !p.B) || (c_bytes && !p.C)) return GEMM_ERR_NULL_PTR;
+  if (overlaps(p.C, c_bytes, p.A, a_bytes) || overlaps(p.C, c_bytes, p.B, b_bytes))
+    return GEMM_ERR_ALIAS;
+  return GEMM_OK;
+}
+
+// The planner's kernel and split for the general form. Copy offsets of an
+// M/N-contiguous operand grow with the K range; when one pass over all of K
+// would not fit in 32 bits, K is cut into passes of *k_pass elements, run
+// one after the other (the second and later with beta = 1), and the plan is
+// made for one pass.
+bool plan_general(const Problem &p, int *kernel, int *split, int *k_pass) {
+  long long k_eff = std::max(p.K, 1);
+  for (int iter = 0; iter < 8; ++iter) {
+    plan(p.M, p.N, static_cast<int>(k_eff), kernel, split, &p);
+    const KernelInfo *k = find_kernel(*kernel);
+    if (!dma_tile_usable(p, k->bm, k->bn, k->bk)) return false;
+    auto fits = [&](long long kc) {
+      const long long span = ceil_div(kc, k->bk) * k->bk + k->bk;
+      return operand_fits(!p.ta, k->bm, p.lda, span) && operand_fits(p.tb, k->bn, p.ldb, span);
+    };
+    long long kp = k_eff;
+    while (!fits(kp) && kp > k->bk) kp = std::max<long long>(k->bk, kp / 2 / k->bk * k->bk);
+    if (!fits(kp)) return false;
+    if (kp >= k_eff) {
+      *k_pass = static_cast<int>(k_eff);
+      return true;
+    }
+    k_eff = kp;
+  }
+  return false;
+}
+
+// Workspace of the general form: the largest of its passes' (the last pass
+// may be shorter and split differently).
+size_t general_workspace(const Problem &p, int kernel, int split, int k_pass) {
+  size_t need = 0;
+  const int lens[2] = {std::min(k_pass, p.K), p.K > k_pass ? p.K % k_pass : 0};
+  for (int len : lens) {
+    Resolved r;
+    if (len > 0 && resolve(p.M, p.N, len, kernel, split, &r))
+      need = std::max(need, workspace_for(p.M, p.N, r));
+  }
+  return need;
+}
+
+int run_general(Problem p, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = validate_general(p);
+  if (st != GEMM_OK) return st;
+  if (p.M == 0 || p.N == 0) return GEMM_OK;
+  int kernel = 0, split = 1, k_pass = std::max(p.K, 1);
+  const bool uses_ab = p.K > 0 && p.alpha != 0.0f;
+  if (uses_ab && !plan_general(p, &kernel, &split, &k_pass)) return GEMM_ERR_INVALID_DIM;
+  const size_t need = uses_ab ? general_workspace(p, kernel, split, k_pass) : 0;
+  const bool own_ws = workspace == nullptr;
+  if (!own_ws && workspace_bytes < need) return GEMM_ERR_WORKSPACE;
+
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != GEMM_OK) return st;
+  if (!uses_ab) return launch_scale_c(p, stream);
+  if (own_ws && need > 0) {
+    workspace = library_workspace(dev, need, &st);
+    if (st != GEMM_OK) return st;
+    if (!workspace) split = 1;   // no workspace available: no split
+  }
+  // K passes: op(A)[:, k0:k0+kp] op(B)[k0:k0+kp, :], accumulated into C.
+  const float beta0 = p.beta;
+  for (int k0 = 0; k0 < p.K; k0 += k_pass) {
+    Problem q = p;
+    q.K = std::min(k_pass, p.K - k0);
+    q.A = p.A + (p.ta ? (long long)k0 * p.lda : k0);
+    q.B = p.B + (p.tb ? k0 : (long long)k0 * p.ldb);
+    q.beta = k0 == 0 ? beta0 : 1.0f;
+    Resolved r;
+    if (!resolve(q.M, q.N, q.K, kernel, split, &r)) return GEMM_ERR_INVALID_PLAN;
+    st = launch(q, r, workspace, stream);
+    if (st != GEMM_OK) return st;
+  }
+  return GEMM_OK;
 }
 
 }  // namespace
@@ -532,6 +722,27 @@ int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, i
                        hipStream_t stream) {
   if (!p) return GEMM_ERR_INVALID_PLAN;
   return run(A, B, C, M, N, K, p, workspace, workspace_bytes, false, stream);
+}
+
+int gemm_f32_general(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                     int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const Problem p{trans_a != 0, trans_b != 0, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+  return run_general(p, workspace, workspace_bytes, stream);
+}
+
+size_t gemm_f32_general_workspace_bytes(int trans_a, int trans_b, int M, int N, int K, int lda,
+                                        int ldb) {
+  // alpha = 1 and C pointer, ldc = N stand-ins: only the plan matters here.
+  const Problem p{trans_a != 0, trans_b != 0, M, N, K, 1.0f, 0.0f, nullptr, nullptr, nullptr,
+                  lda, ldb, std::max(N, 1)};
+  if (M < 0 || N < 0 || K < 0) return 0;
+  const int a_cols = p.ta ? M : K, b_cols = p.tb ? K : N;
+  if (lda < std::max(1, a_cols) || ldb < std::max(1, b_cols)) return 0;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  int kernel = 0, split = 1, k_pass = K;
+  if (!plan_general(p, &kernel, &split, &k_pass)) return 0;
+  return general_workspace(p, kernel, split, k_pass);
 }
 
 const char *gemm_kernel_name(int kernel) {

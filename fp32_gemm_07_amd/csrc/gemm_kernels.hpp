@@ -367,35 +367,38 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// FP32 MFMA kernel fed by direct global -> LDS loads.
+// FP32 MFMA kernel fed by direct global -> LDS copies.
 //
 // gfx950's buffer_load_dwordx4 ... lds copies 16 bytes per lane from global
-// memory straight into LDS (lane i's bytes land at M0 + 16*i; the 4-byte
-// form buffer_load_dword ... lds puts lane i's float at M0 + 4*i), so no data
-// passes through registers: no staging VGPRs, no LDS store instructions, and
-// the wave only waits for a K step's data when it is about to consume it.
-// K steps rotate through NS LDS stages: while step t is being multiplied,
-// steps t+1 .. t+NS-2 are in flight. Each lane's load goes through a buffer
-// resource whose range check turns an out-of-range offset into zeros; lanes
-// whose chunk lies past M, N or the end of the K range get such an offset,
-// which is the zero fill of the edges. The 16-byte copies only need 4-byte
-// aligned sources, so rows of any length are copied this way; a chunk that
-// straddles the end of the K range has its trailing floats zeroed in LDS
-// (zero_k_tail), and chunks straddling the last column of B only feed
-// outputs past N, which are never stored.
+// memory straight into LDS (lane i's bytes land at M0 + 16*i), so no operand
+// data passes through registers: no staging VGPRs, no LDS store
+// instructions, and a wave only waits for a K step's data when it is about
+// to consume it. K steps rotate through NS LDS stages. Each copy goes through
+// a buffer resource whose range check (per dword) turns an out-of-range
+// offset into zeros; lanes whose chunk lies outside the matrix, or past the
+// end of the K range, get such an offset, which is the zero fill of the
+// edges. The 16-byte copies only need 4-byte aligned sources, so rows of any
+// length and any row stride are copied this way; a chunk that straddles the
+// end of the K range in a K-contiguous operand has its trailing floats zeroed
+// in LDS (zero_k_tail), and chunks straddling the last row or column of the
+// output only feed outputs that are never stored.
 //
+// Each operand is stored one of two ways (DmaOperand):
+//   K-contiguous (A as given, or B given transposed): element (x, k) of the
+//     operand at x*ld + k. LDS [BX][BK]; 16-byte chunk c of row x is stored
+//     at chunk c ^ swz_k(x), so the 16-byte fragment reads of 16 consecutive
+//     rows hit distinct banks; a lane's fragment is one 16-byte read of 4
+//     consecutive k.
+//   M/N-contiguous (B as given, or A given transposed): element (x, k) at
+//     k*ld + x. LDS [BK][BX]; the chunks of row k are flipped by
+//     ((k / KS) % NQ) * MI floats, so the NQ lane groups of an instruction,
+//     which read rows KS apart, land MI floats apart, on different banks; a
+//     lane's fragment is four 4-byte reads.
 // Because a copy lands in LDS exactly as the 64 lanes are ordered, rows
-// cannot be padded; instead 16-byte chunks are XOR-swizzled within a row:
-//   A [BM][BK] : chunk c of row r is stored at chunk c ^ swz_a(r), chosen
-//                so that the 16-byte fragment reads of 16 consecutive rows
-//                hit distinct banks;
-//   B [BK][BN] : chunk c of row k is stored at chunk c ^ swb(k),
-//                swb(k) = ((k / KS) % NQ) * (MI / 4), so the NQ lane groups of
-//                an instruction, which read rows KS apart, land MI floats
-//                apart, on different banks.
-// The copies are issued with inline assembly: the compiler does not model
-// the LDS write of its own builtin for this instruction, so the asm carries
-// a memory clobber and the waits (s_waitcnt vmcnt) are explicit.
+// cannot be padded, hence the swizzles. The copies are issued with inline
+// assembly: the compiler does not model the LDS write of its own builtin for
+// this instruction, so the asm carries a memory clobber and the waits
+// (s_waitcnt vmcnt) are explicit.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource: base address, byte range [0, bytes) (each dword of a
@@ -412,19 +415,59 @@ __device__ inline u32x4 make_buffer_rsrc(const void *base, long long bytes) {
 }
 constexpr unsigned kOutOfRange = 0x80000000u;
 
+// The resource and the LDS address are the same for every lane. The
+// compiler's divergence analysis does not always see that (values reached
+// through captured references), and an "s" operand it believes divergent
+// would be given vector registers; readfirstlane states the uniformity
+// (and folds away where the compiler already knows it).
+__device__ inline u32x4 uniform_rsrc(const u32x4 &r) {
+  u32x4 u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+
 // One copy instruction: each lane moves VEC floats (16 or 4 bytes) from
 // rsrc + voffset into LDS at lds_byte_addr + lane * 4 * VEC.
 template <int VEC>
 __device__ inline void dma_copy(const u32x4 &rsrc, unsigned voffset, unsigned lds_byte_addr) {
+  const u32x4 r = uniform_rsrc(rsrc);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte_addr);
   if constexpr (VEC == 4) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(lds_byte_addr), "v"(voffset), "s"(rsrc)
+                 : "s"(m0), "v"(voffset), "s"(r)
                  : "memory");
   } else {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :
-                 : "s"(lds_byte_addr), "v"(voffset), "s"(rsrc)
+                 : "s"(m0), "v"(voffset), "s"(r)
+                 : "memory");
+  }
+}
+
+// The same copy with a per-wave byte offset `soffset` (an SGPR) added to the
+// address. Only used where no lane's chunk crosses the end of the resource
+// range, so the zero fill does not depend on whether the hardware counts
+// soffset in its range check: lanes meant to read zeros carry kOutOfRange in
+// voffset, every other lane reads inside the matrix.
+template <int VEC>
+__device__ inline void dma_copy_soff(const u32x4 &rsrc, unsigned voffset, unsigned soffset,
+                                     unsigned lds_byte_addr) {
+  const u32x4 r = uniform_rsrc(rsrc);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_byte_addr);
+  const unsigned so = __builtin_amdgcn_readfirstlane(soffset);
+  if constexpr (VEC == 4) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(r), "s"(so)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(r), "s"(so)
                  : "memory");
   }
 }
@@ -435,77 +478,164 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC>
+// Swizzle of K-contiguous rows: with 4 chunks per row (BK = 16) 16
+// consecutive rows are told apart by r % 4 (bank quarter) and (r / 4) % 4
+// (chunk); with 8 chunks per row (BK = 32) by r % 2 and (r / 2) % 8.
+template <int CH>
+__device__ inline int swz_k(int r) {
+  return CH == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
+}
+
+// One operand of the copy-fed kernel: BX output rows (A: BX = BM) or columns
+// (B: BX = BN) by a K step of BK, stored K-contiguous (KMAJOR) or
+// M/N-contiguous in global memory, with row stride ld. Per wave: its share of
+// the stage's copy instructions and its fragment read offsets.
+template <int MI, int BX, int BK, int WX, int NW, bool KMAJOR, int VEC>
+struct DmaOperand {
+  static constexpr int NQ = 64 / MI;            // lane groups of an instruction
+  static constexpr int KS = BK / NQ;            // k per lane group per K step
+  static constexpr int NG = KS / 4;             // fragment groups per K step
+  static constexpr int F = WX / MI;             // blocks per wave along x
+  static constexpr int ROW = KMAJOR ? BK : BX;  // floats per LDS row
+  static constexpr int CH = ROW / 4;            // 16-byte chunks per LDS row
+  static constexpr int EP = ROW / VEC;          // lanes per LDS row in one copy
+  static constexpr int RP = 64 / EP;            // LDS rows per copy
+  static constexpr int I = (KMAJOR ? BX : BK) / RP;   // copies per stage
+  static constexpr int L = I / NW;              // copies per wave
+  static constexpr int COPY_BYTES = 256 * VEC;  // LDS bytes one copy fills
+  static constexpr int NRD = KMAJOR ? NG : F;   // fragment read offsets per lane
+  static_assert(VEC == 4 || VEC == 1, "16- or 4-byte copies");
+  static_assert(!KMAJOR || CH == 4 || CH == 8, "K step of 16 or 32");
+  static_assert(EP <= 64 && 64 % EP == 0, "whole LDS rows per copy");
+  static_assert(KMAJOR || BX >= NQ * MI, "column flips stay inside a row");
+  static_assert(I % NW == 0, "copies split evenly over waves");
+
+  unsigned voff[L];  // lane's byte offset from the tile's first element at step 0
+                     // (kOutOfRange when its row or column lies outside the matrix)
+  unsigned lds[L];   // byte offset of the copy within the operand's stage region
+  int kk[L];         // KMAJOR: first k of the lane's chunk; else: its k row
+  bool ok[L];        // row or column inside the matrix
+  int rd[NRD];       // fragment read offsets within the operand's stage region (floats)
+
+  __device__ inline void setup(int lane, int wave, int x0, int X, int ld, int q, int li, int wx) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int n = wave + NW * i;          // copy index within the stage
+      const int r = n * RP + lane / EP;     // LDS row
+      const int pe = (lane % EP) * VEC;     // physical float within the LDS row
+      if constexpr (KMAJOR) {
+        const int ke = ((pe / 4) ^ swz_k<CH>(r)) * 4 + pe % 4;   // logical k
+        ok[i] = x0 + r < X;
+        kk[i] = ke;
+        voff[i] = ok[i] ? (static_cast<unsigned>(r) * static_cast<unsigned>(ld) + ke) * 4u
+                        : kOutOfRange;
+      } else {
+        const int xe = pe ^ (((r / KS) % NQ) * MI);              // logical column
+        ok[i] = x0 + xe < X;
+        kk[i] = r;
+        voff[i] = ok[i] ? (static_cast<unsigned>(r) * static_cast<unsigned>(ld) + xe) * 4u
+                        : kOutOfRange;
+      }
+      lds[i] = static_cast<unsigned>(n * COPY_BYTES);
+    }
+    // For row x = wx*WX + f*MI + li the swizzle swz_k(x) does not depend on f
+    // (f*MI moves x by a multiple of 16 rows), and the columns of lane
+    // group q are flipped by q*MI.
+#pragma unroll
+    for (int j = 0; j < NRD; ++j) {
+      if constexpr (KMAJOR) {
+        const int x = wx * WX + li;
+        rd[j] = x * BK + 4 * (((q * KS + 4 * j) / 4) ^ swz_k<CH>(x));
+      } else {
+        rd[j] = q * KS * BX + ((wx * WX + j * MI + li) ^ (q * MI));
+      }
+    }
+  }
+
+  // Bytes a lane's offset advances per K step.
+  __device__ static inline unsigned step_bytes(int ld) {
+    return KMAJOR ? 4u * BK : 4u * BK * static_cast<unsigned>(ld);
+  }
+
+  // Whether copy i holds data of a K step with kr elements of the range left.
+  __device__ inline bool k_valid(int i, int kr) const { return kk[i] < kr; }
+
+  // Fragment group g of a stage region into frag[F] (4 consecutive k each).
+  __device__ inline void load(const float *region, int g, floatx4 (&frag)[F]) const {
+    if constexpr (KMAJOR) {
+#pragma unroll
+      for (int f = 0; f < F; ++f)
+        frag[f] = *reinterpret_cast<const floatx4 *>(region + rd[g] + f * MI * BK);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int f = 0; f < F; ++f) frag[f][j] = region[rd[f] + (4 * g + j) * BX];
+    }
+  }
+};
+
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC, bool A_KMAJOR,
+          bool B_KMAJOR>
 struct DmaShape {
   static constexpr int NWAVES = WAVES_M * WAVES_N;
-  static constexpr int THREADS = 64 * NWAVES;
   static constexpr int NQ = 64 / MI;
   static constexpr int ACC = MI * MI / 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / MI, FN = WN / MI;
   static constexpr int KS = BK / NQ;
   static constexpr int NG = KS / 4;
-  static constexpr int CA = BK / 4;           // 16-byte chunks per A row (swizzle unit)
-  static constexpr int EPA = BK / VEC;        // copy elements (lanes) per A row
-  static constexpr int RPA = 64 / EPA;        // A rows per copy instruction
-  static constexpr int IA = BM / RPA;         // A copy instructions per stage
-  static constexpr int EPB = BN / VEC;        // copy elements per B row
-  static constexpr int RPB = 64 / EPB;        // B rows per copy instruction
-  static constexpr int IB = BK / RPB;         // B copy instructions per stage
-  static constexpr int LPW = (IA + IB) / NWAVES;  // copies per wave per stage
-  static constexpr int COPY_BYTES = 256 * VEC;    // LDS bytes one copy instruction fills
+  using OpA = DmaOperand<MI, BM, BK, WM, NWAVES, A_KMAJOR, VEC>;
+  using OpB = DmaOperand<MI, BN, BK, WN, NWAVES, B_KMAJOR, VEC>;
+  static constexpr int LPW = OpA::L + OpB::L;     // copies per wave per stage
   static constexpr int A_BYTES = BM * BK * 4;
   static constexpr int STAGE_BYTES = (BM * BK + BK * BN) * 4;
-  static_assert(VEC == 4 || VEC == 1, "16- or 4-byte copies");
-  static_assert(CA == 4 || CA == 8, "K step of 16 or 32");
-  static_assert(EPA <= 64 && 64 % EPA == 0, "whole A rows per copy");
-  static_assert(EPB <= 64 && 64 % EPB == 0 && BN >= 64, "whole B rows per copy");
-  static_assert((IA + IB) % NWAVES == 0 && IA % NWAVES == 0, "copies split evenly over waves");
   static_assert(KS % 4 == 0 && (NG == 1 || NG % 2 == 0), "fragment groups");
   static_assert(NS >= 3 && NS <= 4, "3 or 4 stages");
   static_assert(NS * STAGE_BYTES <= 160 * 1024, "fits LDS");
+  static_assert((NS - 1) * LPW < 64, "vmcnt wait values fit the counter");
+  static_assert(NG % 2 == 0 || NS % 2 == 0, "fragment slots repeat with the stage ring");
 };
 
-// Swizzle of A rows: with 4 chunks per row (BK = 16) 16 consecutive rows are
-// told apart by r % 4 (bank quarter) and (r / 4) % 4 (chunk); with 8 chunks
-// per row (BK = 32) by r % 2 and (r / 2) % 8.
-template <int CA>
-__device__ inline int swz_a(int r) {
-  return CA == 4 ? ((r >> 2) & 3) : ((r >> 1) & 7);
-}
-
+// C <- alpha * op(A) op(B) + beta * C for one output tile (or, with split-K,
+// the partial product of one K range into workspace slab `split`, with
+// alpha = 1, beta = 0 and ldc = N). op(A) is K-contiguous when A_KMAJOR (A
+// given M x K), op(B) when B_KMAJOR (B given N x K, i.e. transposed).
+// beta == 0: C is not read.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC,
-          int WAVES_PER_EU>
+          int WAVES_PER_EU, bool A_KMAJOR, bool B_KMAJOR>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
-                          float *__restrict__ C, int M, int N, int K, int k_chunk,
-                          int tiles_m, int tiles_n, int splits, long long slab) {
-  using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, VEC>;
+                          float *__restrict__ C, int M, int N, int K, int lda, int ldb, int ldc,
+                          float alpha, float beta, int k_chunk, int tiles_m, int tiles_n,
+                          int splits, long long slab) {
+  using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, VEC, A_KMAJOR, B_KMAJOR>;
+  using OpA = typename S::OpA;
+  using OpB = typename S::OpB;
   using Op = Mfma<MI>;
   using acc_t = typename Op::acc_t;
-  constexpr int FM = S::FM, FN = S::FN, KS = S::KS, NG = S::NG, NQ = S::NQ;
-  constexpr int CA = S::CA, EPA = S::EPA, RPA = S::RPA, IA = S::IA, IB = S::IB;
-  constexpr int EPB = S::EPB, RPB = S::RPB, NW = S::NWAVES;
-  constexpr int LA = IA / NW, LB = IB / NW, LPW = LA + LB;   // copies per wave per step
+  constexpr int FM = S::FM, FN = S::FN, NG = S::NG, LPW = S::LPW;
   constexpr int STAGE_F = S::STAGE_BYTES / 4;
-  static_assert(IA % NW == 0 && IB % NW == 0, "every wave copies the same number of A and B chunks");
-  static_assert(NG % 2 == 0 || NS % 2 == 0, "fragment slots repeat with the stage ring");
-  static_assert((NS - 1) * LPW < 64, "vmcnt wait values fit the counter");
-  (void)FM; (void)FN;
 
   __shared__ __attribute__((aligned(16))) float smem[NS * STAGE_F];
   // One real store into the shared array, so the compiler cannot treat it as
   // never written (the copies write it behind the compiler's back).
   if (threadIdx.x == 0) smem[0] = 0.0f;
 
+  // The tile coordinates are uniform; readfirstlane says so to the compiler,
+  // which otherwise keeps the results of the integer divisions of map_tile
+  // in vector registers and everything derived from them (the buffer
+  // resources, the copy bases) with them.
   const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, 8);
-  const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-  const int k_begin = tc.split * k_chunk;
+  const int m0 = __builtin_amdgcn_readfirstlane(tc.tm) * BM;
+  const int n0 = __builtin_amdgcn_readfirstlane(tc.tn) * BN;
+  const int split = __builtin_amdgcn_readfirstlane(tc.split);
+  const int k_begin = split * k_chunk;
   const int k_end = min(K, k_begin + k_chunk);
   const int nk = (k_end - k_begin + BK - 1) / BK;
-  float *__restrict__ Cout = C + (long long)tc.split * slab;
+  float *__restrict__ Cout = C + (long long)split * slab;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -517,70 +647,48 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       static_cast<unsigned>(reinterpret_cast<unsigned long long>(
           (__attribute__((address_space(3))) float *)smem));
 
-  // Copies of this wave, A copy i = workgroup copy wave + NW*i of the IA A
-  // copies of a stage, likewise for B. Per copy and lane: byte offset from the
-  // K step's base (already replaced by kOutOfRange when the row of A or the
-  // column of B lies outside the matrix), the k it covers, and the copy's
-  // byte offset within a stage (uniform).
-  unsigned a_voff[LA], a_lds[LA];
-  int a_k[LA];
-  bool a_ok[LA];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int n = wave + NW * i;
-    const int r = n * RPA + lane / EPA;             // row within the tile
-    const int pe = (lane % EPA) * VEC;              // physical float within the row
-    const int ke = ((pe / 4) ^ swz_a<CA>(r)) * 4 + pe % 4;   // logical k within the step
-    a_ok[i] = m0 + r < M;
-    a_k[i] = ke;
-    a_voff[i] = a_ok[i] ? (static_cast<unsigned>(r) * static_cast<unsigned>(K) + ke) * 4u
-                        : kOutOfRange;
-    a_lds[i] = static_cast<unsigned>(n * S::COPY_BYTES);
-  }
-  unsigned b_voff[LB], b_lds[LB];
-  int b_k[LB];
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int n = wave + NW * i;
-    const int k = n * RPB + lane / EPB;             // row of B within the step
-    const int pe = (lane % EPB) * VEC;
-    const int ne = pe ^ (((k / KS) % NQ) * MI);     // logical column within the tile
-    b_k[i] = k;
-    b_voff[i] = (n0 + ne < N) ? (static_cast<unsigned>(k) * static_cast<unsigned>(N) + ne) * 4u
-                              : kOutOfRange;
-    b_lds[i] = static_cast<unsigned>(S::A_BYTES + n * S::COPY_BYTES);
-  }
+  OpA opa;
+  OpB opb;
+  opa.setup(lane, wave, m0, M, lda, q, li, wm);
+  opb.setup(lane, wave, n0, N, ldb, q, li, wn);
 
   // One buffer resource per operand for the whole K range: base at the
-  // tile's first element, range ending exactly at the end of A (B), so a
-  // chunk running past the last element of a matrix reads zeros there. Step
-  // s adds s*BK floats (A) or s*BK rows (B) to each lane's offset; the host
-  // keeps every valid offset below 2^31 (BM*K*4 and k_chunk*N*4 bytes), and
+  // tile's first element, range ending exactly at the operand's last element,
+  // so a chunk running past it reads zeros. Step s adds s times a constant
+  // to each lane's offset; the host keeps every valid offset below 2^31, and
   // offsets that start at kOutOfRange stay past the range.
-  const long long a_first = (long long)m0 * K + k_begin, b_first = (long long)k_begin * N + n0;
-  const u32x4 ra = make_buffer_rsrc(A + a_first, 4 * ((long long)M * K - a_first));
-  const u32x4 rb = make_buffer_rsrc(B + b_first, 4 * ((long long)K * N - b_first));
-  const unsigned a_step_bytes = 4u * BK;
-  const unsigned b_step_bytes = 4u * BK * static_cast<unsigned>(N);
-  // Copies of a step whose K range is whole (every step but the last).
+  const long long a_first = A_KMAJOR ? (long long)m0 * lda + k_begin : (long long)k_begin * lda + m0;
+  const long long a_end = A_KMAJOR ? (long long)(M - 1) * lda + K : (long long)(K - 1) * lda + M;
+  const long long b_first = B_KMAJOR ? (long long)n0 * ldb + k_begin : (long long)k_begin * ldb + n0;
+  const long long b_end = B_KMAJOR ? (long long)(N - 1) * ldb + K : (long long)(K - 1) * ldb + N;
+  const u32x4 ra = make_buffer_rsrc(A + a_first, 4 * (a_end - a_first));
+  const u32x4 rb = make_buffer_rsrc(B + b_first, 4 * (b_end - b_first));
+  const unsigned a_step = OpA::step_bytes(lda), b_step = OpB::step_bytes(ldb);
+  // Copies of a step whose K range is whole and not the last: no chunk
+  // crosses the end of an operand, so the step's advance goes in soffset and
+  // the lane offsets stay loop-invariant (no vector add in front of a copy).
   auto issue_full = [&](int step, unsigned stage_byte) {
-    const unsigned da = a_step_bytes * step, db = b_step_bytes * step;
+    const unsigned da = a_step * step, db = b_step * step;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) dma_copy<VEC>(ra, a_voff[i] + da, stage_byte + a_lds[i]);
+    for (int i = 0; i < OpA::L; ++i)
+      dma_copy_soff<VEC>(ra, opa.voff[i], da, stage_byte + opa.lds[i]);
 #pragma unroll
-    for (int i = 0; i < LB; ++i) dma_copy<VEC>(rb, b_voff[i] + db, stage_byte + b_lds[i]);
+    for (int i = 0; i < OpB::L; ++i)
+      dma_copy_soff<VEC>(rb, opb.voff[i], db, stage_byte + S::A_BYTES + opb.lds[i]);
   };
   // Copies of any step: chunks past the end of the K range read zeros.
   auto issue_checked = [&](int step) {
     const int kr = k_end - (k_begin + step * BK);   // K elements left in this step
-    const unsigned da = a_step_bytes * step, db = b_step_bytes * step;
+    const unsigned da = a_step * step, db = b_step * step;
     const unsigned stage_byte = smem_base + static_cast<unsigned>((step % NS) * S::STAGE_BYTES);
 #pragma unroll
-    for (int i = 0; i < LA; ++i)
-      dma_copy<VEC>(ra, a_k[i] < kr ? a_voff[i] + da : kOutOfRange, stage_byte + a_lds[i]);
+    for (int i = 0; i < OpA::L; ++i)
+      dma_copy<VEC>(ra, opa.k_valid(i, kr) ? opa.voff[i] + da : kOutOfRange,
+                    stage_byte + opa.lds[i]);
 #pragma unroll
-    for (int i = 0; i < LB; ++i)
-      dma_copy<VEC>(rb, b_k[i] < kr ? b_voff[i] + db : kOutOfRange, stage_byte + b_lds[i]);
+    for (int i = 0; i < OpB::L; ++i)
+      dma_copy<VEC>(rb, opb.k_valid(i, kr) ? opb.voff[i] + db : kOutOfRange,
+                    stage_byte + S::A_BYTES + opb.lds[i]);
   };
   // Wait until this wave's copies of a step have landed while the copies of
   // `later` steps issued after it may stay in flight (vmcnt counts this
@@ -594,49 +702,42 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     wait_vmcnt<0>();
   };
   auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
-  // When the K range does not end on a 16-byte chunk, the A chunk of each
-  // row that straddles its end also brought in up to three floats past it
-  // (the start of the next row). Once this wave's copies of the last step
-  // have landed, it zeroes those floats in the chunks it copied itself.
+  // When the K range does not end on a 16-byte chunk, the chunk of each
+  // K-contiguous row that straddles its end also brought in up to three
+  // floats past it (the row's padding or the next row). Once this wave's
+  // copies of the last step have landed, it zeroes those floats in the chunks
+  // it copied itself.
   auto zero_k_tail = [&](int step) {
-    if constexpr (VEC == 4) {
+    if constexpr (VEC == 4 && (A_KMAJOR || B_KMAJOR)) {
       const int kr = k_end - (k_begin + step * BK);
       if (step != nk - 1 || kr % 4 == 0) return;
       float *stage = smem + (step % NS) * STAGE_F;
+      if constexpr (A_KMAJOR) {
 #pragma unroll
-      for (int i = 0; i < LA; ++i) {
-        if (a_ok[i] && a_k[i] < kr && a_k[i] + 4 > kr) {
-          float *dst = stage + a_lds[i] / 4 + lane * 4;
-          for (int e = kr - a_k[i]; e < 4; ++e) dst[e] = 0.0f;
+        for (int i = 0; i < OpA::L; ++i) {
+          if (opa.ok[i] && opa.kk[i] < kr && opa.kk[i] + 4 > kr) {
+            float *dst = stage + opa.lds[i] / 4 + lane * 4;
+            for (int e = kr - opa.kk[i]; e < 4; ++e) dst[e] = 0.0f;
+          }
+        }
+      }
+      if constexpr (B_KMAJOR) {
+#pragma unroll
+        for (int i = 0; i < OpB::L; ++i) {
+          if (opb.ok[i] && opb.kk[i] < kr && opb.kk[i] + 4 > kr) {
+            float *dst = stage + S::A_BYTES / 4 + opb.lds[i] / 4 + lane * 4;
+            for (int e = kr - opb.kk[i]; e < 4; ++e) dst[e] = 0.0f;
+          }
         }
       }
     }
   };
 
-  // Fragment reads. Per lane the read offsets within a stage are fixed: for
-  // A row r = wm*WM + fm*MI + li the swizzle swz_a(r) does not depend on fm
-  // (fm*MI moves r by a multiple of 8 rows, or of 16 with CA = 8), and the
-  // B columns of lane group q are flipped by q*MI.
-  int a_rd[NG], b_rd[FN];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int r = wm * S::WM + li;
-    a_rd[g] = r * BK + 4 * (((q * KS + 4 * g) / 4) ^ swz_a<CA>(r));
-  }
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn)
-    b_rd[fn] = BM * BK + q * KS * BN + ((wn * S::WN + fn * MI + li) ^ (q * MI));
-
   floatx4 fa[2][FM];
-  float fb[2][FN][4];
+  floatx4 fb[2][FN];
   auto load_frags = [&](const float *st, int g, int slot) {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-      fa[slot][fm] = *reinterpret_cast<const floatx4 *>(st + a_rd[g] + fm * MI * BK);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) fb[slot][fn][j] = st[b_rd[fn] + (4 * g + j) * BN];
+    opa.load(st, g, fa[slot]);
+    opb.load(st + S::A_BYTES / 4, g, fb[slot]);
   };
 
   acc_t acc[FM][FN];
@@ -758,18 +859,32 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     if (t + 1 < nk) k_step_tail(t + 1, std::integral_constant<int, 1>());
   }
 
+  // Epilogue: accumulator v of block (fm, fn) is output row Op::row(q, v) and
+  // column li of that block. beta is uniform; the branch on it is taken once.
+  auto store_tile = [&](auto beta_is_zero) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+    for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int col = n0 + wn * S::WN + fn * MI + li;
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = n0 + wn * S::WN + fn * MI + li;
 #pragma unroll
-      for (int v = 0; v < S::ACC; ++v) {
-        const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
-        if (row < M && col < N) Cout[(long long)row * N + col] = acc[fm][fn][v];
+        for (int v = 0; v < S::ACC; ++v) {
+          const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
+          if (row < M && col < N) {
+            float *p = Cout + (long long)row * ldc + col;
+            if constexpr (decltype(beta_is_zero)::value)
+              *p = alpha * acc[fm][fn][v];
+            else
+              *p = __builtin_fmaf(alpha, acc[fm][fn][v], beta * *p);
+          }
+        }
       }
     }
-  }
+  };
+  if (beta == 0.0f)
+    store_tile(std::true_type());
+  else
+    store_tile(std::false_type());
 }
 
 // ---------------------------------------------------------------------------
@@ -838,36 +953,55 @@ void valu_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K reduction: C[e] = ws[0][e] + ws[1][e] + ... + ws[S-1][e], always in
-// ascending slab order, so the result does not depend on which workgroup
-// finished first. Pure streaming: S*M*N reads and M*N writes, HBM bound.
+// Split-K reduction: sum_s ws[s][e] in ascending slab order (so the result
+// does not depend on which workgroup finished first), then
+// C <- alpha * sum + beta * C (C not read when beta == 0). The slabs are
+// dense M x N; C has row stride ldc. V = 4: four consecutive columns per
+// lane (N and ldc multiples of 4, 16-byte aligned). Pure streaming:
+// S*M*N reads and M*N writes (plus M*N reads when beta != 0), HBM bound.
 template <int V>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void splitk_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, long long count,
-                          int splits) {
+                          int N, int ldc, int splits, float alpha, float beta) {
   const long long stride = (long long)gridDim.x * kThreads;
+  const bool dense = ldc == N;
   for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e * V < count; e += stride) {
+    const long long first = e * V;
+    float *out = dense ? C + first : C + (first / N) * ldc + first % N;
     if constexpr (V == 4) {
-      floatx4 s = *reinterpret_cast<const floatx4 *>(ws + e * 4);
+      floatx4 s = *reinterpret_cast<const floatx4 *>(ws + first);
       for (int p = 1; p < splits; ++p) {
-        const floatx4 v = *reinterpret_cast<const floatx4 *>(ws + (long long)p * count + e * 4);
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(ws + (long long)p * count + first);
         s[0] = s[0] + v[0]; s[1] = s[1] + v[1]; s[2] = s[2] + v[2]; s[3] = s[3] + v[3];
       }
-      *reinterpret_cast<floatx4 *>(C + e * 4) = s;
+      floatx4 r;
+      if (beta == 0.0f) {
+        r[0] = alpha * s[0]; r[1] = alpha * s[1]; r[2] = alpha * s[2]; r[3] = alpha * s[3];
+      } else {
+        const floatx4 c = *reinterpret_cast<const floatx4 *>(out);
+        r[0] = __builtin_fmaf(alpha, s[0], beta * c[0]);
+        r[1] = __builtin_fmaf(alpha, s[1], beta * c[1]);
+        r[2] = __builtin_fmaf(alpha, s[2], beta * c[2]);
+        r[3] = __builtin_fmaf(alpha, s[3], beta * c[3]);
+      }
+      *reinterpret_cast<floatx4 *>(out) = r;
     } else {
-      float s = ws[e];
-      for (int p = 1; p < splits; ++p) s = s + ws[(long long)p * count + e];
-      C[e] = s;
+      float s = ws[first];
+      for (int p = 1; p < splits; ++p) s = s + ws[(long long)p * count + first];
+      *out = beta == 0.0f ? alpha * s : __builtin_fmaf(alpha, s, beta * *out);
     }
   }
 }
 
-// Fill C with +0.0 (the K = 0 product).
+// C <- beta * C over M x N with row stride ldc, +0.0 when beta == 0 (C then
+// not read): the whole result when K = 0 or alpha = 0.
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
-void fill_zero_kernel(float *__restrict__ C, long long count) {
+void scale_c_kernel(float *__restrict__ C, long long count, int N, int ldc, float beta) {
   const long long stride = (long long)gridDim.x * kThreads;
-  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < count; e += stride)
-    C[e] = 0.0f;
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < count; e += stride) {
+    float *out = ldc == N ? C + e : C + (e / N) * ldc + e % N;
+    *out = beta == 0.0f ? 0.0f : beta * *out;
+  }
 }
 
 }  // namespace gemm

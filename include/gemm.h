@@ -143,6 +143,46 @@ int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, i
                        const gemm_plan_t *plan, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* The general form, with the argument order of the BLAS SGEMM call of the
+ * yekq.top LeetGPU walkthrough's cuBLAS reference section, for row-major
+ * storage:
+ *
+ *   C <- alpha * op(A) * op(B) + beta * C,   op(A) M x K, op(B) K x N, C M x N
+ *
+ *   trans_a == 0: A is stored M x K, element (i, k) at A[i*lda + k], lda >= K;
+ *   trans_a != 0: A is stored K x M (op(A) = A^T), element (i, k) of op(A) at
+ *                 A[k*lda + i], lda >= M;
+ *   trans_b == 0: B is stored K x N, element (k, j) at B[k*ldb + j], ldb >= N;
+ *   trans_b != 0: B is stored N x K, element (k, j) of op(B) at B[j*ldb + k],
+ *                 ldb >= K;
+ *   element (i, j) of C at C[i*ldc + j], ldc >= N. Every leading dimension is
+ *   at least 1. Elements between a row's end and its stride are neither read
+ *   (A, B, C) nor written (C).
+ *
+ * BLAS conventions: beta == 0 means C is not read (NaN there does not
+ * propagate); alpha == 0 or K == 0 means A and B are not read (and may be
+ * null) and C <- beta * C (+0.0 when beta == 0). The sum is in FP32 as for
+ * gemm_f32; then alpha * sum + beta * c is one FP32 fused multiply-add.
+ * alpha = 1, beta = 0, no transposes and dense strides give bit-for-bit the
+ * result of gemm_f32 with the same plan.
+ *
+ * workspace: null to use the library's per-device split-K workspace (as
+ * gemm_f32), else a caller-owned buffer of at least
+ * gemm_f32_general_workspace_bytes(...) bytes (GEMM_ERR_WORKSPACE if
+ * smaller). A, B, C overlapping: C's extent (first to last element) must not
+ * overlap A's or B's (GEMM_ERR_ALIAS). Operands whose rows are so long that
+ * one 64-row tile spans 2^31 bytes are rejected (GEMM_ERR_INVALID_DIM);
+ * an operand whose K range would span 2^31 bytes is processed in several
+ * K passes, each after the first accumulating into C. Returns a status. */
+int gemm_f32_general(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
+                     int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes gemm_f32_general needs for these shapes and strides
+ * (0 when it needs none, or for invalid arguments). */
+size_t gemm_f32_general_workspace_bytes(int trans_a, int trans_b, int M, int N, int K, int lda,
+                                        int ldb);
+
 /* Static, human-readable name of a kernel id ("unknown" otherwise). */
 const char *gemm_kernel_name(int kernel);
 

@@ -131,3 +131,51 @@ def test_status_strings_and_names():
         assert binding.gemm_kernel_name(k) not in ("unknown", "auto")
     assert binding.gemm_kernel_name(0) == "auto"
     assert isinstance(binding.gemm_last_hip_error(), int)
+
+
+# ---------------------------------------------------------------------------
+# gemm_f32_general: argument checks (all before any HIP call).
+
+def _gst(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws=None, wsb=0):
+    f = ctypes.c_float
+    return binding.raw_status("gemm_f32_general", ta, tb, M, N, K, f(alpha), A, lda, B, ldb,
+                              f(beta), C, ldc, ws, wsb, None)
+
+
+def test_general_leading_dimensions_checked():
+    A, B, C = VP(0x7f0000000000), VP(0x7f1000000000), VP(0x7f2000000000)
+    E = binding.GEMM_ERR_INVALID_DIM
+    assert _gst(0, 0, 4, 5, 6, 1, A, 5, B, 5, 0, C, 5) == E        # lda < K
+    assert _gst(1, 0, 4, 5, 6, 1, A, 3, B, 5, 0, C, 5) == E        # transposed A: lda < M
+    assert _gst(0, 0, 4, 5, 6, 1, A, 6, B, 4, 0, C, 5) == E        # ldb < N
+    assert _gst(0, 1, 4, 5, 6, 1, A, 6, B, 5, 0, C, 5) == E        # transposed B: ldb < K
+    assert _gst(0, 0, 4, 5, 6, 1, A, 6, B, 5, 0, C, 4) == E        # ldc < N
+    assert _gst(0, 0, -1, 5, 6, 1, A, 6, B, 5, 0, C, 5) == E
+    # a 64-row tile of a K-contiguous A would span 2^31 bytes: rejected
+    assert _gst(0, 0, 64, 64, 16, 1, A, 1 << 23, B, 64, 0, C, 64) == E
+
+
+def test_general_pointer_rules():
+    A, B, C = VP(0x7f0000000000), VP(0x7f1000000000), VP(0x7f2000000000)
+    assert _gst(0, 0, 4, 5, 6, 1, None, 6, B, 5, 0, C, 5) == binding.GEMM_ERR_NULL_PTR
+    assert _gst(0, 0, 4, 5, 6, 1, A, 6, None, 5, 0, C, 5) == binding.GEMM_ERR_NULL_PTR
+    assert _gst(0, 0, 4, 5, 6, 1, A, 6, B, 5, 0, None, 5) == binding.GEMM_ERR_NULL_PTR
+    # nothing to produce: no pointer needed
+    assert _gst(0, 0, 0, 5, 6, 1, None, 6, None, 5, 0, None, 5) == binding.GEMM_OK
+    # C's extent (with its stride) overlapping A's
+    base = 0x7f0000000000
+    st = _gst(0, 0, 4, 4, 4, 1, VP(base), 4, B, 4, 0, VP(base + 4 * 4 * 3), 8)
+    assert st == binding.GEMM_ERR_ALIAS
+
+
+def test_general_workspace_checked():
+    M, N, K = 256, 256, 8192
+    need = binding.gemm_f32_general_workspace_bytes(0, 0, M, N, K, K, N)
+    assert need > 0 and need == binding.gemm_f32_workspace_bytes(M, N, K)
+    A, B, C = VP(0x7f0000000000), VP(0x7f1000000000), VP(0x7f2000000000)
+    st = _gst(0, 0, M, N, K, 1, A, K, B, N, 0, C, N, VP(0x7f3000000000), need - 4)
+    assert st == binding.GEMM_ERR_WORKSPACE
+    # transposed operands and strides: workspace is still 4 * S * M * N
+    need_t = binding.gemm_f32_general_workspace_bytes(1, 1, M, N, K, M + 3, K + 5)
+    assert need_t % (4 * M * N) == 0
+    assert binding.gemm_f32_general_workspace_bytes(0, 0, M, N, K, K - 1, N) == 0   # bad lda
