@@ -860,31 +860,53 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   }
 
   // Epilogue: accumulator v of block (fm, fn) is output row Op::row(q, v) and
-  // column li of that block. beta is uniform; the branch on it is taken once.
-  auto store_tile = [&](auto beta_is_zero) {
+  // column li of that block. The branches on beta and on whether the tile
+  // lies wholly inside C are uniform and taken once: interior tiles store
+  // without per-element checks, and with beta != 0 the C values of a block
+  // row are all loaded before any is used, so their latencies overlap.
+  auto store_tile = [&](auto beta_is_zero, auto checked) {
+    constexpr bool kBetaZero = decltype(beta_is_zero)::value;
+    constexpr bool kChecked = decltype(checked)::value;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
+      float cv[FN][S::ACC];
+      if constexpr (!kBetaZero) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = n0 + wn * S::WN + fn * MI + li;
+#pragma unroll
+          for (int v = 0; v < S::ACC; ++v) {
+            const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
+            const bool in = !kChecked || (row < M && col < N);
+            cv[fn][v] = in ? Cout[(long long)row * ldc + col] : 0.0f;
+          }
+        }
+      }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int col = n0 + wn * S::WN + fn * MI + li;
 #pragma unroll
         for (int v = 0; v < S::ACC; ++v) {
           const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
-          if (row < M && col < N) {
+          if (!kChecked || (row < M && col < N)) {
             float *p = Cout + (long long)row * ldc + col;
-            if constexpr (decltype(beta_is_zero)::value)
+            if constexpr (kBetaZero)
               *p = alpha * acc[fm][fn][v];
             else
-              *p = __builtin_fmaf(alpha, acc[fm][fn][v], beta * *p);
+              *p = __builtin_fmaf(alpha, acc[fm][fn][v], beta * cv[fn][v]);
           }
         }
       }
     }
   };
-  if (beta == 0.0f)
-    store_tile(std::true_type());
-  else
-    store_tile(std::false_type());
+  const bool interior = m0 + BM <= M && n0 + BN <= N;
+  if (beta == 0.0f) {
+    if (interior) store_tile(std::true_type(), std::false_type());
+    else store_tile(std::true_type(), std::true_type());
+  } else {
+    if (interior) store_tile(std::false_type(), std::false_type());
+    else store_tile(std::false_type(), std::true_type());
+  }
 }
 
 // ---------------------------------------------------------------------------

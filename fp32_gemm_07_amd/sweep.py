@@ -2,6 +2,7 @@
 
     python -m fp32_gemm_07_amd.sweep [MxKxN ...]
     python -m fp32_gemm_07_amd.sweep --ladder
+    python -m fp32_gemm_07_amd.sweep --orders [MxKxN ...]
 
 For each shape: the planner's choice, torch.matmul in FP32 (the vendor
 library, for context), and the four fastest (kernel, split) plans, each the
@@ -12,6 +13,10 @@ the measurement the planner's cost model is fitted to.
 --ladder times the optimisation ladder of the yekq.top LeetGPU walkthrough
 (v0 .. v4, then the matrix-core kernels) on its two shapes, 1024 x 512 x 1024
 and 1001 x 513 x 777, with the mean of 50 launches as in its tables.
+
+--orders times gemm_f32_general for the four transpose cases, with
+alpha = 1, beta = 0 and with alpha = 2, beta = 0.5, next to torch.matmul on
+the same (transposed) storage.
 """
 from __future__ import annotations
 
@@ -86,11 +91,68 @@ def ladder(np, torch) -> int:
     return 0
 
 
+ORDER_SHAPES = ["4096x4096x4096", "1024x512x1024", "1001x513x777", "2048x1024x2048",
+                "512x131072x512"]
+
+
+def orders(np, torch, shapes) -> int:
+    """gemm_f32_general for every transpose case, and with alpha, beta, next to
+    torch.matmul on the same storage (transposed views)."""
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.rand((2048, 2048), device="cuda", generator=gen)
+    for _ in range(100):
+        torch.matmul(x, x)
+    torch.cuda.synchronize()
+    torch.backends.cuda.matmul.allow_tf32 = False
+    for shape in shapes:
+        M, K, N = (int(v) for v in shape.split("x"))
+        flop = roofline.gemm_flops(M, N, K)
+        reps = max(5, min(200, int(0.15 / max(flop / 120e12, 1e-6))))
+
+        def timeit(call):
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                call()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+        C = torch.rand((M, N), device="cuda", generator=gen)
+        for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            A = torch.rand((K, M) if ta else (M, K), device="cuda", generator=gen)
+            B = torch.rand((N, K) if tb else (K, N), device="cuda", generator=gen)
+            lda, ldb = A.shape[1], B.shape[1]
+            need = binding.gemm_f32_general_workspace_bytes(ta, tb, M, N, K, lda, ldb)
+            ws = torch.empty(max(need // 4, 1), device="cuda")
+            res = []
+            for alpha, beta in ((1.0, 0.0), (2.0, 0.5)):
+                us = timeit(lambda: binding.gemm_f32_general(ta, tb, M, N, K, alpha, A, lda, B, ldb,
+                                                             beta, C, N, ws, need,
+                                                             stream.cuda_stream))
+                res.append(us)
+            opA = A.t() if ta else A
+            opB = B.t() if tb else B
+            t_v = timeit(lambda: torch.matmul(opA, opB, out=C))
+            case = "NT"[ta] + "NT"[tb]
+            print(f"{shape} {case}: alpha=1,beta=0 {res[0]:.1f} us ({flop / res[0] / 1e6:.1f} TF) | "
+                  f"alpha=2,beta=0.5 {res[1]:.1f} us ({flop / res[1] / 1e6:.1f} TF) | "
+                  f"vendor {t_v:.1f} us ({flop / t_v / 1e6:.1f} TF)", flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     import numpy as np
     import torch
     if argv and argv[0] == "--ladder":
         return ladder(np, torch)
+    if argv and argv[0] == "--orders":
+        return orders(np, torch, argv[1:] or ORDER_SHAPES)
     shapes = [tuple(int(x) for x in s.split("x")) for s in (argv or DEFAULT_SHAPES)]
     stream = torch.cuda.current_stream()
     gen = torch.Generator(device="cuda").manual_seed(0)
