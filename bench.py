@@ -41,8 +41,8 @@ FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196734.0, "write_kib": 65536.0,
-        "kernel_source_sha256": "9661b26330233a10eb1191fd7a59db46ff1264a63bf3f9d8eadf39281c39a4f3",
+        "fetch_kib": 196736.5, "write_kib": 65536.0,
+        "kernel_source_sha256": "3730c4a6c94ca46c2ba16bf746870276cd09f2ba1c4e281152d98c07ee58c40a",
     },
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
