@@ -8,10 +8,11 @@
 // gfx950-specific here:
 //   - the per-lane register tile of the pages becomes the accumulator of
 //     v_mfma_f32_32x32x2_f32 (a 32x32 FP32 block per wave per instruction);
-//   - LDS is double buffered, so one barrier per K step guards both the
-//     read-after-write and the write-after-read hazard the lesson's two
-//     barriers guard (section 3): at step t waves read buffer t%2 and fill
-//     buffer (t+1)%2, and the barrier at the end of step t orders both;
+//   - one barrier per K step guards both the read-after-write and the
+//     write-after-read hazard the lesson's two barriers guard (section 3):
+//     the register-staged kernel double-buffers LDS (at step t waves read
+//     buffer t%2 and fill buffer (t+1)%2), the copy-fed kernel rotates a ring
+//     of 3 or 4 stages filled by direct global -> LDS copies;
 //   - every lane stays alive to every barrier; out-of-range elements are
 //     loaded as 0.0f and out-of-range outputs are skipped at the store;
 //   - workgroup -> tile mapping is aware of the 8 XCDs (see map_tile);
@@ -77,8 +78,7 @@ __device__ inline TileCoord map_tile(int bid, int tiles_m, int tiles_n, int spli
 // share a CU, one per SIMD.
 //   MI = 32: v_mfma_f32_32x32x2_f32 (32x2 by 2x32, 16 accumulators per lane);
 //   MI = 16: v_mfma_f32_16x16x4_f32 (16x4 by 4x16, 4 accumulators per lane).
-// Both retire 256 FLOP per clock per CU; on MI355X the chip holds a higher
-// clock under the 16x16 form, so the planner prefers it for large products.
+// Both retire 256 FLOP per clock per CU.
 //
 // Operand layout (CDNA3/CDNA4 ISA, matrix instructions): the 64 lanes form
 // NQ = 64/MI groups q = lane / MI of MI lanes each; lane (q, i) supplies
