@@ -31,19 +31,14 @@ GEMM_KERNEL_MFMA_128x128 = 3
 GEMM_KERNEL_MFMA_64x64 = 4
 GEMM_KERNEL_MFMA_256x256_W8 = 5
 GEMM_KERNEL_VALU_64x64 = 10
-GEMM_KERNEL_MFMA16_256x256 = 11
-GEMM_KERNEL_MFMA16_256x256_W8 = 12
 GEMM_KERNEL_MFMA16_256x128 = 13
 GEMM_KERNEL_MFMA16_128x128 = 14
 GEMM_KERNEL_MFMA16_64x64 = 15
-GEMM_KERNEL_MFMA16_256x256_K16 = 16
 GEMM_KERNEL_MFMA16_128x128_K16 = 17
 GEMM_KERNEL_MFMA16_256x128_K16 = 18
 GEMM_KERNEL_MFMA_128x128_W1 = 19
-GEMM_KERNEL_MFMA16_128x128_W1 = 20
 GEMM_KERNEL_MFMA_64x64_W1 = 21
 GEMM_KERNEL_DMA32_256x256_W8 = 30
-GEMM_KERNEL_DMA16_256x256_W8 = 32
 GEMM_KERNEL_DMA32_128x128_W4 = 33
 GEMM_KERNEL_DMA16_128x128_W4 = 34
 GEMM_KERNEL_DMA32_256x256_W8_S3 = 35
@@ -61,19 +56,14 @@ KERNELS = {
     "mfma32_256x128": GEMM_KERNEL_MFMA_256x128,
     "mfma32_128x128": GEMM_KERNEL_MFMA_128x128,
     "mfma32_64x64": GEMM_KERNEL_MFMA_64x64,
-    "mfma16_256x256": GEMM_KERNEL_MFMA16_256x256,
-    "mfma16_256x256_w8": GEMM_KERNEL_MFMA16_256x256_W8,
     "mfma16_256x128": GEMM_KERNEL_MFMA16_256x128,
     "mfma16_128x128": GEMM_KERNEL_MFMA16_128x128,
     "mfma16_64x64": GEMM_KERNEL_MFMA16_64x64,
-    "mfma16_256x256_k16": GEMM_KERNEL_MFMA16_256x256_K16,
     "mfma16_128x128_k16": GEMM_KERNEL_MFMA16_128x128_K16,
     "mfma16_256x128_k16": GEMM_KERNEL_MFMA16_256x128_K16,
     "mfma32_128x128_w1": GEMM_KERNEL_MFMA_128x128_W1,
-    "mfma16_128x128_w1": GEMM_KERNEL_MFMA16_128x128_W1,
     "mfma32_64x64_w1": GEMM_KERNEL_MFMA_64x64_W1,
     "dma32_256x256_w8": GEMM_KERNEL_DMA32_256x256_W8,
-    "dma16_256x256_w8": GEMM_KERNEL_DMA16_256x256_W8,
     "dma32_128x128_w4": GEMM_KERNEL_DMA32_128x128_W4,
     "dma16_128x128_w4": GEMM_KERNEL_DMA16_128x128_W4,
     "dma32_256x256_w8_s3": GEMM_KERNEL_DMA32_256x256_W8_S3,

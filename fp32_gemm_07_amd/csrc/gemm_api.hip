@@ -39,20 +39,15 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_MFMA_256x128, 256, 128, 16, "mfma32_f32_256x128x16"},
     {GEMM_KERNEL_MFMA_128x128, 128, 128, 16, "mfma32_f32_128x128x16"},
     {GEMM_KERNEL_MFMA_64x64, 64, 64, 16, "mfma32_f32_64x64x16"},
-    {GEMM_KERNEL_MFMA16_256x256, 256, 256, 32, "mfma16_f32_256x256x32"},
-    {GEMM_KERNEL_MFMA16_256x256_W8, 256, 256, 32, "mfma16_f32_256x256x32_w8"},
     {GEMM_KERNEL_MFMA16_256x128, 256, 128, 32, "mfma16_f32_256x128x32"},
     {GEMM_KERNEL_MFMA16_128x128, 128, 128, 32, "mfma16_f32_128x128x32"},
     {GEMM_KERNEL_MFMA16_64x64, 64, 64, 32, "mfma16_f32_64x64x32"},
-    {GEMM_KERNEL_MFMA16_256x256_K16, 256, 256, 16, "mfma16_f32_256x256x16"},
     {GEMM_KERNEL_MFMA16_128x128_K16, 128, 128, 16, "mfma16_f32_128x128x16"},
     {GEMM_KERNEL_MFMA16_256x128_K16, 256, 128, 16, "mfma16_f32_256x128x16"},
     {GEMM_KERNEL_MFMA_128x128_W1, 128, 128, 16, "mfma32_f32_128x128x16_w1"},
-    {GEMM_KERNEL_MFMA16_128x128_W1, 128, 128, 16, "mfma16_f32_128x128x16_w1"},
     {GEMM_KERNEL_MFMA_64x64_W1, 64, 64, 16, "mfma32_f32_64x64x16_w1"},
     {GEMM_KERNEL_VALU_64x64, 64, 64, 16, "valu_f32_64x64x16"},
     {GEMM_KERNEL_DMA32_256x256_W8, 256, 256, 16, "dma_mfma32_f32_256x256x16_w8_s4"},
-    {GEMM_KERNEL_DMA16_256x256_W8, 256, 256, 16, "dma_mfma16_f32_256x256x16_w8_s4"},
     {GEMM_KERNEL_DMA32_128x128_W4, 128, 128, 16, "dma_mfma32_f32_128x128x16_w4_s4"},
     {GEMM_KERNEL_DMA16_128x128_W4, 128, 128, 16, "dma_mfma16_f32_128x128x16_w4_s4"},
     {GEMM_KERNEL_DMA32_256x256_W8_S3, 256, 256, 16, "dma_mfma32_f32_256x256x16_w8_s3"},
@@ -373,13 +368,6 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
     case GEMM_KERNEL_MFMA_64x64:
       launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
       return true;
-    case GEMM_KERNEL_MFMA16_256x256:
-      launch_mfma<16, 256, 256, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return true;
-    case GEMM_KERNEL_MFMA16_256x256_W8:
-      if (!launch_mfma<16, 256, 256, 32, 2, 4, 2, false>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<16, 256, 256, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return true;
     case GEMM_KERNEL_MFMA16_256x128:
       launch_mfma<16, 256, 128, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
       return true;
@@ -389,9 +377,6 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
     case GEMM_KERNEL_MFMA16_64x64:
       launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
       return true;
-    case GEMM_KERNEL_MFMA16_256x256_K16:
-      launch_mfma<16, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return true;
     case GEMM_KERNEL_MFMA16_128x128_K16:
       launch_mfma<16, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
       return true;
@@ -400,9 +385,6 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
       return true;
     case GEMM_KERNEL_MFMA_128x128_W1:
       launch_mfma<32, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
-      return true;
-    case GEMM_KERNEL_MFMA16_128x128_W1:
-      launch_mfma<16, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_64x64_W1:
       launch_mfma<32, 64, 64, 16, 1, 1, 2, true>(A, B, out, M, N, K, r, slab, stream);
@@ -414,10 +396,6 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
       return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, out, ldo, alpha, beta, r, slab,
                                                             stream) ||
-             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
-    case GEMM_KERNEL_DMA16_256x256_W8:
-      return launch_dma<16, 256, 256, 16, 2, 4, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                             stream) ||
              (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
     case GEMM_KERNEL_DMA32_128x128_W4:
       return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,

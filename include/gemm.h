@@ -70,22 +70,17 @@ enum {
   GEMM_KERNEL_MFMA_64x64 = 4,      /* mfma32, 64x64 tile, K step 16, 4 waves of 32x32 */
   GEMM_KERNEL_MFMA_256x256_W8 = 5, /* mfma32, 256x256 tile, K step 16, 8 waves of 128x64 */
   GEMM_KERNEL_VALU_64x64 = 10,     /* vector FMA, 64x64 tile, K step 16, 4x4 outputs per lane */
-  GEMM_KERNEL_MFMA16_256x256 = 11,    /* mfma16, 256x256 tile, K step 32, 4 waves of 128x128 */
-  GEMM_KERNEL_MFMA16_256x256_W8 = 12, /* mfma16, 256x256 tile, K step 32, 8 waves of 128x64 */
   GEMM_KERNEL_MFMA16_256x128 = 13,    /* mfma16, 256x128 tile, K step 32, 4 waves of 128x64 */
   GEMM_KERNEL_MFMA16_128x128 = 14,    /* mfma16, 128x128 tile, K step 32, 4 waves of 64x64 */
   GEMM_KERNEL_MFMA16_64x64 = 15,      /* mfma16, 64x64 tile, K step 32, 4 waves of 32x32 */
-  GEMM_KERNEL_MFMA16_256x256_K16 = 16, /* mfma16, 256x256 tile, K step 16, 4 waves of 128x128 */
   GEMM_KERNEL_MFMA16_128x128_K16 = 17, /* mfma16, 128x128 tile, K step 16, 4 waves of 64x64 */
   GEMM_KERNEL_MFMA16_256x128_K16 = 18, /* mfma16, 256x128 tile, K step 16, 4 waves of 128x64 */
   GEMM_KERNEL_MFMA_128x128_W1 = 19,    /* mfma32, 128x128 tile, K step 16, one wave */
-  GEMM_KERNEL_MFMA16_128x128_W1 = 20,  /* mfma16, 128x128 tile, K step 16, one wave */
   GEMM_KERNEL_MFMA_64x64_W1 = 21,      /* mfma32, 64x64 tile, K step 16, one wave */
   /* Kernels fed by direct global->LDS copies through a ring of LDS stages
    * (any K and N; shapes whose per-tile offsets would pass 2^31 bytes run the
    * register-staged kernel of the same tile). */
   GEMM_KERNEL_DMA32_256x256_W8 = 30,    /* mfma32, 256x256, K step 16, 8 waves, 4 stages */
-  GEMM_KERNEL_DMA16_256x256_W8 = 32,    /* mfma16, 256x256, K step 16, 8 waves, 4 stages */
   GEMM_KERNEL_DMA32_128x128_W4 = 33,    /* mfma32, 128x128, K step 16, 4 waves, 4 stages */
   GEMM_KERNEL_DMA16_128x128_W4 = 34,    /* mfma16, 128x128, K step 16, 4 waves, 4 stages */
   GEMM_KERNEL_DMA32_256x256_W8_S3 = 35, /* mfma32, 256x256, K step 16, 8 waves, 3 stages */
