@@ -187,3 +187,64 @@ def test_general_k_passes_for_long_strided_rows():
     del dBbig
     ref, S = oracle.gemm_general(0, 0, M, N, K, 1.0, X, K, Y, N, 0.5, C0, N)
     assert_within_bound(got, ref.reshape(M, N), S, "K passes")
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+def test_general_guard_bands_misaligned(ta, tb):
+    """A, B and C, each shifted by one float (4-byte aligned only) and with
+    padded rows, inside one NaN-filled buffer with NaN guards around each:
+    a read outside an operand turns outputs into NaN, a write outside C's
+    M x N elements changes a NaN that must stay."""
+    t = torch()
+    M, K, N = 97, 53, 71
+    say(f"general guard bands {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=70 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=71)[0]
+    A, lda = stored(X, ta, 3)
+    B, ldb = stored(Y, tb, 2)
+    Cs, ldc = stored(C0, False, 5)
+    g = 257
+    offA = g
+    offB = offA + A.size + g
+    offC = offB + B.size + g
+    total = offC + Cs.size + g
+    host = np.full(total, np.nan, np.float32)
+    host[offA:offA + A.size] = A
+    host[offB:offB + B.size] = B
+    host[offC:offC + Cs.size] = Cs
+    buf = to_dev(host)
+    base = buf.data_ptr()
+    binding.gemm_f32_general(ta, tb, M, N, K, 1.25, base + 4 * offA, lda, base + 4 * offB, ldb,
+                             -0.75, base + 4 * offC, ldc)
+    t.cuda.synchronize()
+    out = buf.cpu().numpy()
+    ref, S = oracle.gemm_general(ta, tb, M, N, K, 1.25, A, lda, B, ldb, -0.75, Cs, ldc)
+    check(out[offC:offC + Cs.size], ref, S, M, N, ldc, "guarded general")
+    guards = np.concatenate([out[:offA], out[offA + A.size:offB], out[offB + B.size:offC],
+                             out[offC + Cs.size:]])
+    assert np.isnan(guards).all()
+    np.testing.assert_array_equal(out[offA:offA + A.size], A)
+    np.testing.assert_array_equal(out[offB:offB + B.size], B)
+
+
+@pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)], ids=["TN", "NT", "TT"])
+def test_general_full_size_sampled(ta, tb):
+    """4096^3 in the transposed orders through the planner's 256 x 256 kernel:
+    3000 sampled outputs against the oracle (the plain oracle's entries on the
+    explicitly transposed operands, which the general form's pins tie to it),
+    every output finite."""
+    t = torch()
+    M = N = K = 4096
+    say(f"general full size {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "normal", seed=80 + ta + 2 * tb)
+    dA = to_dev(np.ascontiguousarray(X.T) if ta else X)
+    dB = to_dev(np.ascontiguousarray(Y.T) if tb else Y)
+    dC = nan_buffer(M * N)
+    binding.gemm_f32_general(ta, tb, M, N, K, 1.0, dA, M if ta else K, dB, K if tb else N, 0.0,
+                             dC, N)
+    t.cuda.synchronize()
+    C = dC.cpu().numpy().reshape(M, N)
+    assert np.isfinite(C).all()
+    rows, cols = gemm_inputs.sample_indices(M, N, 3000, seed=ta + 2 * tb)
+    ref, S = oracle.gemm_entries(X, Y, rows, cols)
+    assert_within_bound(C[rows, cols], ref, S, "general 4096^3 sampled")

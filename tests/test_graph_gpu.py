@@ -1,0 +1,67 @@
+"""Library calls captured into a HIP graph (through torch.cuda.graph) and
+replayed: every replay must equal the eager result bit for bit.
+
+The entry points with caller-owned workspaces (gemm_f32_ex,
+gemm_f32_with_plan, gemm_f32_general with a workspace) make no allocation
+and no memset, so they can be captured; the split-K case captures the
+partial-product kernel and the reduction. Between replays the test runs
+eager work of its own and synchronises, and it changes the inputs in place
+so a replay that reused stale results would be caught.
+"""
+import numpy as np
+import pytest
+
+import gemm_inputs
+from fp32_gemm_07_amd import binding
+from gpu_util import say, to_dev, torch
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(1001, 513, 777, "plain"), (256, 8192, 256, "plain"), (300, 513, 260, "general")]
+
+
+@pytest.mark.parametrize("M,K,N,form", CASES, ids=[f"{m}x{k}x{n}-{f}" for m, k, n, f in CASES])
+def test_graph_replays_match_eager(M, K, N, form):
+    t = torch()
+    say(f"graph capture {M}x{K}x{N} {form}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=M + K + N)
+    dA, dB = to_dev(X), to_dev(Y)
+    dC = t.empty((M, N), dtype=t.float32, device="cuda:0")
+    if form == "plain":
+        need = binding.gemm_f32_workspace_bytes(M, N, K)
+    else:
+        need = binding.gemm_f32_general_workspace_bytes(1, 0, M, N, K, M, N)
+        dA = to_dev(np.ascontiguousarray(X.T))   # op(A) = A^T, A stored K x M
+    ws = t.empty((max(need // 4, 1),), dtype=t.float32, device="cuda:0")
+
+    def call(stream_handle):
+        if form == "plain":
+            binding.gemm_f32_ex(dA, dB, dC, M, N, K, ws, need, stream_handle)
+        else:
+            binding.gemm_f32_general(1, 0, M, N, K, 1.5, dA, M, dB, N, 0.0, dC, N, ws, need,
+                                     stream_handle)
+
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        call(side.cuda_stream)           # warm-up outside capture
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        call(t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+
+    for r in range(4):
+        # new inputs in place, eager reference, then a replay on the same inputs
+        dA.mul_(-1.0 if r % 2 else 0.5)
+        dB.add_(0.25)
+        call(t.cuda.current_stream().cuda_stream)
+        t.cuda.synchronize()
+        eager = dC.clone()
+        dC.fill_(float("nan"))
+        graph.replay()
+        t.cuda.synchronize()
+        assert t.equal(dC.view(t.int32), eager.view(t.int32)), f"replay {r}"
+        assert t.isfinite(dC).all()
