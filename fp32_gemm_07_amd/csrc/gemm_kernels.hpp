@@ -503,7 +503,11 @@ struct DmaOperand {
   static constexpr int I = (KMAJOR ? BX : BK) / RP;   // copies per stage
   static constexpr int L = I / NW;              // copies per wave
   static constexpr int COPY_BYTES = 256 * VEC;  // LDS bytes one copy fills
-  static constexpr int NRD = KMAJOR ? NG : F;   // fragment read offsets per lane
+  // M/N-contiguous with 4 blocks per wave: block f takes rows (or columns)
+  // x = 4*i + f of the wave's range instead of f*MI + i, so a lane's four
+  // values at one k are adjacent and one 16-byte read fetches them.
+  static constexpr bool INTERLEAVE = !KMAJOR && F == 4;
+  static constexpr int NRD = KMAJOR ? NG : (INTERLEAVE ? 1 : F);   // read offsets per lane
   static_assert(VEC == 4 || VEC == 1, "16- or 4-byte copies");
   static_assert(!KMAJOR || CH == 4 || CH == 8, "K step of 16 or 32");
   static_assert(EP <= 64 && 64 % EP == 0, "whole LDS rows per copy");
@@ -546,11 +550,16 @@ struct DmaOperand {
       if constexpr (KMAJOR) {
         const int x = wx * WX + li;
         rd[j] = x * BK + 4 * (((q * KS + 4 * j) / 4) ^ swz_k<CH>(x));
+      } else if constexpr (INTERLEAVE) {
+        rd[j] = q * KS * BX + ((wx * WX + 4 * li) ^ (q * MI));
       } else {
         rd[j] = q * KS * BX + ((wx * WX + j * MI + li) ^ (q * MI));
       }
     }
   }
+
+  // Offset, within the wave's x range, of value i of block f.
+  __device__ static constexpr int x_of(int f, int i) { return INTERLEAVE ? 4 * i + f : f * MI + i; }
 
   // Bytes a lane's offset advances per K step.
   __device__ static inline unsigned step_bytes(int ld) {
@@ -566,6 +575,13 @@ struct DmaOperand {
 #pragma unroll
       for (int f = 0; f < F; ++f)
         frag[f] = *reinterpret_cast<const floatx4 *>(region + rd[g] + f * MI * BK);
+    } else if constexpr (INTERLEAVE) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(region + rd[0] + (4 * g + j) * BX);
+#pragma unroll
+        for (int f = 0; f < F; ++f) frag[f][j] = v[f];
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -873,10 +889,10 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       if constexpr (!kBetaZero) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          const int col = n0 + wn * S::WN + fn * MI + li;
+          const int col = n0 + wn * S::WN + OpB::x_of(fn, li);
 #pragma unroll
           for (int v = 0; v < S::ACC; ++v) {
-            const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
+            const int row = m0 + wm * S::WM + OpA::x_of(fm, Op::row(q, v));
             const bool in = !kChecked || (row < M && col < N);
             cv[fn][v] = in ? Cout[(long long)row * ldc + col] : 0.0f;
           }
@@ -884,10 +900,10 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int col = n0 + wn * S::WN + fn * MI + li;
+        const int col = n0 + wn * S::WN + OpB::x_of(fn, li);
 #pragma unroll
         for (int v = 0; v < S::ACC; ++v) {
-          const int row = m0 + wm * S::WM + fm * MI + Op::row(q, v);
+          const int row = m0 + wm * S::WM + OpA::x_of(fm, Op::row(q, v));
           if (!kChecked || (row < M && col < N)) {
             float *p = Cout + (long long)row * ldc + col;
             if constexpr (kBetaZero)

@@ -248,3 +248,18 @@ def test_general_full_size_sampled(ta, tb):
     rows, cols = gemm_inputs.sample_indices(M, N, 3000, seed=ta + 2 * tb)
     ref, S = oracle.gemm_entries(X, Y, rows, cols)
     assert_within_bound(C[rows, cols], ref, S, "general 4096^3 sampled")
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+def test_general_large_tile_ragged(ta, tb):
+    """A ragged shape whose plan is the 256 x 256 kernel (its transposed-A
+    form reads interleaved rows): every output against the oracle, with
+    alpha, beta and padded strides."""
+    M, K, N = 4001, 77, 3999
+    plan = binding.gemm_f32_plan(M, N, K)
+    assert binding.gemm_kernel_name(plan.kernel).startswith("dma_mfma32_f32_256x256")
+    say(f"general 256-tile ragged {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=90 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=91)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=(2, 3, 1))
+    check(got, ref, S, M, N, ldc, "256-tile ragged general")
