@@ -41,8 +41,8 @@ FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196736.5, "write_kib": 65536.0,
-        "kernel_source_sha256": "3730c4a6c94ca46c2ba16bf746870276cd09f2ba1c4e281152d98c07ee58c40a",
+        "fetch_kib": 196736.125, "write_kib": 65536.0,
+        "kernel_source_sha256": "69587c7895895c5d95f1631bb221e29625fbe117198bd1ba1359015e33d603a5",
     },
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
