@@ -162,9 +162,13 @@ constexpr double kReduceFixedUs = 6.0;
 constexpr double kMaxWorkspaceBytes = 1024.0 * 1024.0 * 1024.0;
 constexpr double kHbmBytesPerUs = 5.0e6;
 
-double plan_cost_us(int M, int N, int K, const PlanCandidate &c, int split, int *splits_out) {
+// A (kernel, split) whose copy offsets would not fit in 32 bits is not
+// considered (the launch would fall back to a slower kernel or K passes).
+double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, int *splits_out) {
+  const int M = pr.M, N = pr.N, K = pr.K;
   Resolved r;
   if (!resolve(M, N, K, c.kernel, split, &r)) return 1e30;
+  if (!dma_fits(pr, r.k->bm, r.k->bn, r.k->bk, r.k_chunk)) return 1e30;
   const double wg = static_cast<double>(r.tiles_m * r.tiles_n * r.splits);
   const double per_cu = std::ceil(wg / kNumCus);
   const double flop = 2.0 * r.k->bm * r.k->bn * static_cast<double>(r.k_chunk);
@@ -185,6 +189,8 @@ void plan(int M, int N, int K, int *kernel, int *split, const Problem *general =
   *kernel = kPlanCandidates[0].kernel;
   *split = 1;
   double best = 1e30;
+  Problem pr = general ? *general : plain_problem(nullptr, nullptr, nullptr, M, N, K);
+  pr.K = K;
   for (const PlanCandidate &c : kPlanCandidates) {
     if (general) {
       const KernelInfo *k = find_kernel(c.kernel);
@@ -192,8 +198,8 @@ void plan(int M, int N, int K, int *kernel, int *split, const Problem *general =
     }
     for (int s = 1; s <= 64; s *= 2) {
       if (s > 1 && K / s < 256) break;   // each K range keeps >= 256 elements
-      int launched = 1;
-      const double us = plan_cost_us(M, N, K, c, s, &launched);
+      int launched = s;
+      const double us = plan_cost_us(pr, c, s, &launched);
       if (launched < s) break;           // fewer K steps than ranges asked for
       // Ties (within 1%) go to the candidate seen first: bigger tiles, fewer splits.
       if (us < best * 0.99) {

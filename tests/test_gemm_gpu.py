@@ -234,3 +234,54 @@ def test_splitk_deterministic_and_matches_unsplit_on_integers():
     A, B = gemm_inputs.draw(M, K, N, "uniform", seed=9)
     plan = binding.make_plan(binding.GEMM_KERNEL_MFMA_128x128, 7)
     assert_bits_equal(run(A, B, plan=plan), run(A, B, plan=plan), "rerun")
+
+
+# ---------------------------------------------------------------------------
+# Degenerate and large-operand shapes through the planner.
+
+SKINNY = [(1, 4096, 4096), (4096, 4096, 1), (4096, 1, 4096), (1, 131072, 1), (3, 70000, 5)]
+
+
+@pytest.mark.parametrize("M,K,N", SKINNY, ids=[f"{m}x{k}x{n}" for m, k, n in SKINNY])
+def test_skinny_and_outer_products(M, K, N):
+    """Vector x matrix, matrix x vector, the K = 1 outer product and long dot
+    products, with the planner's plan (split K where it chooses to)."""
+    say(f"skinny {M}x{K}x{N} plan {binding.gemm_f32_plan(M, N, K)}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=M + K + N)
+    C = run(A, B)
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, f"{M}x{K}x{N}")
+
+
+def test_operand_past_2gib_offsets():
+    """B of 2 GiB (32768 x 16384): an unsplit copy-fed launch would need copy
+    offsets past 2^31 bytes, so that plan runs the register-staged kernel of
+    the same tile; the planner's own plan (split K) and the general form
+    (K passes if needed) run copy-fed. All three against sampled oracle
+    entries, and the planner's and the fallback's agree within the bound."""
+    t = torch()
+    M, K, N = 256, 32768, 16384
+    say(f"2 GiB operand {M}x{K}x{N}")
+    A, B = gemm_inputs.draw(M, K, N, "normal", seed=99)
+    dA, dB = to_dev(A), to_dev(B)
+    rows, cols = gemm_inputs.sample_indices(M, N, 2000, seed=5)
+    ref, S = oracle.gemm_entries(A, B, rows, cols)
+    del B
+    s = t.cuda.current_stream()
+    outs = {}
+    for name, plan in (("fallback", binding.make_plan(binding.GEMM_KERNEL_DMA32_256x256_W8_S3, 1)),
+                       ("planner", binding.gemm_f32_plan(M, N, K))):
+        need = binding.gemm_f32_plan_workspace_bytes(M, N, K, plan)
+        ws = t.empty((max(need // 4, 1),), dtype=t.float32, device="cuda:0")
+        dC = nan_buffer(M * N)
+        binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, ws, need, s.cuda_stream)
+        s.synchronize()
+        outs[name] = dC.cpu().numpy().reshape(M, N)
+        del ws, dC
+    dC = nan_buffer(M * N)
+    binding.gemm_f32_general(0, 0, M, N, K, 1.0, dA, K, dB, N, 0.0, dC, N, stream=s.cuda_stream)
+    s.synchronize()
+    outs["general"] = dC.cpu().numpy().reshape(M, N)
+    for name, C in outs.items():
+        assert np.isfinite(C).all(), name
+        assert_within_bound(C[rows, cols], ref, S, name)
