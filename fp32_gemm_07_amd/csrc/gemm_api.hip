@@ -399,44 +399,54 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
     case GEMM_KERNEL_DMA32_256x256_W8:
       return launch_dma<32, 256, 256, 16, 2, 4, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
                                                              stream) ||
-             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab,
+                                                                    stream));
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
       return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, out, ldo, alpha, beta, r, slab,
                                                             stream) ||
-             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab,
+                                                                    stream));
     case GEMM_KERNEL_DMA32_128x128_W4:
       return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
                                                             stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                    stream));
     case GEMM_KERNEL_DMA16_128x128_W4:
       return launch_dma<16, 128, 128, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
                                                              stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                    stream));
     case GEMM_KERNEL_DMA16_64x64:
       return launch_dma<16, 64, 64, 32, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
                                                            stream) ||
-             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                  stream));
     case GEMM_KERNEL_DMA32_64x64:
       return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,
                                                           stream) ||
-             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                  stream));
     case GEMM_KERNEL_DMA16_128x64:
       return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
                                                             stream) ||
-             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                  stream));
     case GEMM_KERNEL_DMA32_128x128_W8:
       return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,
                                                             stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream));
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                    stream));
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
       if (exact)
         hipLaunchKernelGGL(gemm::valu_gemm_kernel<false>, grid, dim3(gemm::kThreads), 0, stream, A,
-                           B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
+                           B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits,
+                           slab);
       else
         hipLaunchKernelGGL(gemm::valu_gemm_kernel<true>, grid, dim3(gemm::kThreads), 0, stream, A,
-                           B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
+                           B, out, M, N, K, r.k_chunk, (int)r.tiles_m, (int)r.tiles_n, r.splits,
+                           slab);
       return true;
     }
     case GEMM_KERNEL_LADDER_V0:
