@@ -55,6 +55,7 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_DMA32_64x64, 64, 64, 16, "dma_mfma32_f32_64x64x16_w4_s4"},
     {GEMM_KERNEL_DMA16_128x64, 128, 64, 32, "dma_mfma16_f32_128x64x32_w4_s4"},
     {GEMM_KERNEL_DMA32_128x128_W8, 128, 128, 16, "dma_mfma32_f32_128x128x16_w8_s4"},
+    {GEMM_KERNEL_DMA32_64x64_S3, 64, 64, 16, "dma_mfma32_f32_64x64x16_w4_s3"},
     {GEMM_KERNEL_LADDER_V0, 16, 16, 16, "ladder_v0_naive_rows_along_lanes"},
     {GEMM_KERNEL_LADDER_V1, 16, 16, 16, "ladder_v1_naive_cols_along_lanes"},
     {GEMM_KERNEL_LADDER_V2, 16, 16, 16, "ladder_v2_lds_16x16x16"},
@@ -154,7 +155,7 @@ struct PlanCandidate {
 constexpr PlanCandidate kPlanCandidates[] = {
     {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6},
     {GEMM_KERNEL_DMA32_128x128_W8, 0.982, 6.9, 3.9},
-    {GEMM_KERNEL_DMA32_64x64, 0.91, 1.2, 6.5},
+    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
@@ -355,8 +356,9 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
   const int M = p.M, N = p.N, K = p.K;
   const bool plain = !p.ta && !p.tb && p.lda == K && p.ldb == N && ldo == N && alpha == 1.0f &&
                      beta == 0.0f;
-  const bool dma_kernel = r.k->id >= GEMM_KERNEL_DMA32_256x256_W8 &&
-                          r.k->id <= GEMM_KERNEL_DMA32_128x128_W8;
+  const bool dma_kernel = (r.k->id >= GEMM_KERNEL_DMA32_256x256_W8 &&
+                           r.k->id <= GEMM_KERNEL_DMA32_128x128_W8) ||
+                          r.k->id == GEMM_KERNEL_DMA32_64x64_S3;
   if (!plain && !dma_kernel) return false;
   switch (r.k->id) {
     case GEMM_KERNEL_MFMA_256x256:
@@ -422,7 +424,7 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
              (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA32_64x64:
-      return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,
+      return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
                                                           stream) ||
              (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                   stream));
@@ -436,6 +438,11 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
                                                             stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
+    case GEMM_KERNEL_DMA32_64x64_S3:
+      return launch_dma<32, 64, 64, 16, 2, 2, 3, 2, true>(p, out, ldo, alpha, beta, r, slab,
+                                                           stream) ||
+             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                  stream));
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));

@@ -32,7 +32,7 @@ DEFAULT_SHAPES = [
 ]
 KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4", "dma32_128x128_w8",
            "dma16_128x128_w4",
-           "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64", "mfma32_128x128",
+           "dma32_64x64_s3", "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64", "mfma32_128x128",
            "mfma32_64x64", "valu_64x64"]
 SPLITS = (1, 2, 4, 8, 16, 32, 64)
 MAX_WORKSPACE = 2 << 30
@@ -44,7 +44,7 @@ LADDER = [("v0 naive, lanes along rows", "ladder_v0"), ("v1 naive, lanes along c
           ("v2 LDS tiles 16x16", "ladder_v2"), ("v3 LDS, 4 outputs per lane", "ladder_v3"),
           ("v4 LDS, 4x4 outputs per lane", "valu_64x64"),
           ("MFMA 32x32x2, register-staged 64x64", "mfma32_64x64"),
-          ("MFMA 32x32x2, copy-fed 64x64", "dma32_64x64")]
+          ("MFMA 32x32x2, copy-fed 64x64", "dma32_64x64_s3")]
 
 
 def ladder(np, torch) -> int:

@@ -88,6 +88,7 @@ enum {
   GEMM_KERNEL_DMA32_64x64 = 37,         /* mfma32, 64x64, K step 16, 4 waves, 4 stages */
   GEMM_KERNEL_DMA16_128x64 = 38,        /* mfma16, 128x64, K step 32, 4 waves, 4 stages */
   GEMM_KERNEL_DMA32_128x128_W8 = 39,    /* mfma32, 128x128, K step 16, 8 waves of 64x32, 4 stages */
+  GEMM_KERNEL_DMA32_64x64_S3 = 45,      /* mfma32, 64x64, K step 16, 4 waves, 3 stages */
   /* The optimisation ladder of the yekq.top LeetGPU walkthrough (sections v0
    * to v3; its v4 is GEMM_KERNEL_VALU_64x64), for comparison only. */
   GEMM_KERNEL_LADDER_V0 = 40,  /* one output per lane, lanes along rows (uncoalesced), 16x16 */

@@ -104,9 +104,9 @@ def test_planner_choices_for_standing_workloads():
     assert p5.k_chunk % 16 == 0
     # few output tiles and a long K: small tiles, K split
     p = binding.gemm_f32_plan(1024, 1024, 4096)
-    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3
     p = binding.gemm_f32_plan(256, 256, 8192)
-    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64 and p.split_k > 1
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_k > 1
     # 24 x 24 tiles of 256 would leave a third round 25% full: 128x128 tiles
     p = binding.gemm_f32_plan(6144, 6144, 6144)
     assert p.kernel == binding.GEMM_KERNEL_DMA32_128x128_W8 and p.split_k == 1
