@@ -41,8 +41,8 @@ FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196736.125, "write_kib": 65536.0,
-        "kernel_source_sha256": "69587c7895895c5d95f1631bb221e29625fbe117198bd1ba1359015e33d603a5",
+        "fetch_kib": 196729.5, "write_kib": 65536.0,
+        "kernel_source_sha256": "33efb740eb4f8235b03fa66d293337b55935697f4a9545f57735ce800d0ea9a9",
     },
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
@@ -203,7 +203,9 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": w.name, "M": M, "N": N, "K": K, "dist": w.dist, "seed": w.seed,
-            "plan": {"kernel": kname, "split_k": plan.split_k if args.kernel == "auto" else args.split},
+            "plan": {"kernel": kname,
+                     "split_k": plan.split_k if args.kernel == "auto" else args.split,
+                     "split_tail": bool(plan.split_tail)},
             "parallelism": "1 GPU",
         },
         "pct_of_fp32_peak": round(100 * value / peak, 2),

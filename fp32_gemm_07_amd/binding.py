@@ -101,11 +101,11 @@ class GemmError(RuntimeError):
 
 class gemm_plan_t(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("split_k", ctypes.c_int),
-                ("k_chunk", ctypes.c_int), ("reserved", ctypes.c_int)]
+                ("k_chunk", ctypes.c_int), ("split_tail", ctypes.c_int)]
 
     def __repr__(self):
         return (f"gemm_plan_t(kernel={gemm_kernel_name(self.kernel)}, split_k={self.split_k}, "
-                f"k_chunk={self.k_chunk})")
+                f"k_chunk={self.k_chunk}, split_tail={self.split_tail})")
 
 
 _lib = None
@@ -205,8 +205,10 @@ def gemm_f32_plan(M: int, N: int, K: int) -> gemm_plan_t:
     return p
 
 
-def make_plan(kernel: int, split_k: int = 1) -> gemm_plan_t:
-    return gemm_plan_t(kernel, split_k, 0, 0)
+def make_plan(kernel: int, split_k: int = 1, split_tail: bool = False) -> gemm_plan_t:
+    """An explicit plan; split_tail splits only the tiles of the last, partial
+    round of 256 (copy-fed kernels only)."""
+    return gemm_plan_t(kernel, split_k, 0, int(split_tail))
 
 
 def gemm_f32_plan_workspace_bytes(M: int, N: int, K: int, plan: gemm_plan_t) -> int:

@@ -70,26 +70,49 @@ const KernelInfo *find_kernel(int id) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// The kernels fed by direct global -> LDS copies (the only ones that take a
+// split tail).
+bool is_dma_kernel(int id) {
+  return (id >= GEMM_KERNEL_DMA32_256x256_W8 && id <= GEMM_KERNEL_DMA32_128x128_W8) ||
+         id == GEMM_KERNEL_DMA32_64x64_S3;
+}
+
 struct Resolved {
   const KernelInfo *k;
-  int splits;     // number of K ranges actually launched (>= 1)
+  int splits;     // number of K ranges of a split tile (>= 1)
   int k_chunk;    // length of each K range
   long long tiles_m, tiles_n;
+  long long dp_tiles;   // tiles computed whole before the split ones (split tail), else 0
+  int K;
+  // K elements one workgroup covers at most (its copy offsets grow with it).
+  long long k_span() const { return dp_tiles > 0 ? K : k_chunk; }
+  long long workgroups() const { return dp_tiles + (tiles_m * tiles_n - dp_tiles) * splits; }
 };
 
-// Turn (kernel, requested split) into launch geometry. The split is clamped
-// to the number of K steps; every range then holds at least one element.
-bool resolve(int M, int N, int K, int kernel, int split_req, Resolved *out) {
+// Turn (kernel, requested split, split tail) into launch geometry. The split
+// is clamped to the number of K steps; every range then holds at least one
+// element. A split tail keeps the tiles of whole rounds of kNumCus tiles
+// unsplit (with a whole number of rounds nothing is split).
+bool resolve(int M, int N, int K, int kernel, int split_req, bool split_tail, Resolved *out) {
   const KernelInfo *k = find_kernel(kernel);
   if (!k || split_req < 1) return false;
+  if (split_tail && !is_dma_kernel(kernel)) return false;
   out->k = k;
   out->tiles_m = ceil_div(M, k->bm);
   out->tiles_n = ceil_div(N, k->bn);
+  out->dp_tiles = 0;
+  out->K = K;
   const long long ksteps = std::max<long long>(1, ceil_div(K, k->bk));
   const long long s = std::min<long long>(split_req, ksteps);
   const long long chunk = ceil_div(ceil_div(std::max(K, 1), s), k->bk) * k->bk;
   out->k_chunk = static_cast<int>(std::min<long long>(chunk, INT_MAX));
   out->splits = static_cast<int>(K > 0 ? ceil_div(K, out->k_chunk) : 1);
+  if (split_tail && out->splits > 1) {
+    const long long tiles = out->tiles_m * out->tiles_n;
+    const long long dp = tiles / kNumCus * kNumCus;
+    if (dp == tiles) return resolve(M, N, K, kernel, 1, false, out);
+    out->dp_tiles = dp;
+  }
   return true;
 }
 
@@ -141,11 +164,12 @@ bool dma_tile_usable(const Problem &p, int bm, int bn, int bk) {
 //   n * (2 * BM * BN * k_chunk / (rate_cu * eff) + per_wg) + fixed
 // with rate_cu = 256 FLOP/clk at 2.38 GHz and eff, per_wg (prologue and
 // epilogue of one workgroup) and fixed (launch, clock skew between XCDs)
-// per kernel below. Splitting K adds the partial sums (S slabs written and
-// read, C written), which stay in the last-level cache at these sizes,
-// at about 8 TB/s plus a fixed cost for the extra launch; and no launch is
-// cheaper than moving A, B and C once at about 5 TB/s. Workspace is capped
-// at 1 GiB.
+// per kernel below. With a split tail each CU takes dp_tiles / CUs whole
+// tiles, then its share of the split ones. Splitting K adds the partial sums
+// of the split tiles (S slabs written and read, C written), which stay in
+// the last-level cache at these sizes, at about 8 TB/s plus a fixed cost for
+// the extra launch; and no launch is cheaper than moving A, B and C once at
+// about 5 TB/s. Workspace is capped at 1 GiB.
 struct PlanCandidate {
   int kernel;
   double eff;
@@ -165,30 +189,42 @@ constexpr double kHbmBytesPerUs = 5.0e6;
 
 // A (kernel, split) whose copy offsets would not fit in 32 bits is not
 // considered (the launch would fall back to a slower kernel or K passes).
-double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, int *splits_out) {
+// *r_out: the geometry costed.
+double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool tail,
+                    Resolved *r_out) {
   const int M = pr.M, N = pr.N, K = pr.K;
-  Resolved r;
-  if (!resolve(M, N, K, c.kernel, split, &r)) return 1e30;
-  if (!dma_fits(pr, r.k->bm, r.k->bn, r.k->bk, r.k_chunk)) return 1e30;
-  const double wg = static_cast<double>(r.tiles_m * r.tiles_n * r.splits);
-  const double per_cu = std::ceil(wg / kNumCus);
-  const double flop = 2.0 * r.k->bm * r.k->bn * static_cast<double>(r.k_chunk);
-  double us = per_cu * (flop / (kRateCuFlopPerUs * c.eff) + c.per_wg_us) + c.fixed_us;
+  Resolved &r = *r_out;
+  if (!resolve(M, N, K, c.kernel, split, tail, &r)) return 1e30;
+  if (!dma_fits(pr, r.k->bm, r.k->bn, r.k->bk, r.k_span())) return 1e30;
+  const double tile_flop = 2.0 * r.k->bm * r.k->bn;
+  const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * c.eff) + c.per_wg_us;
+  const double split_tiles = static_cast<double>(r.tiles_m * r.tiles_n - r.dp_tiles);
+  double us = std::ceil(split_tiles * r.splits / kNumCus) * per_wg + c.fixed_us;
+  if (r.dp_tiles > 0)
+    us += static_cast<double>(r.dp_tiles / kNumCus) *
+          (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * c.eff) +
+           c.per_wg_us);
   if (r.splits > 1) {
     const double slab = 4.0 * M * static_cast<double>(N);
     if (slab * r.splits > kMaxWorkspaceBytes) return 1e30;
-    us += (2.0 * r.splits + 1.0) * slab / kReduceBytesPerUs + kReduceFixedUs;
+    const double split_bytes =
+        r.dp_tiles > 0 ? 4.0 * split_tiles * r.k->bm * r.k->bn : slab;
+    us += (2.0 * r.splits + 1.0) * split_bytes / kReduceBytesPerUs + kReduceFixedUs;
   }
   // No launch beats reading A and B and writing C once (about 5 TB/s).
   const double bytes = 4.0 * (static_cast<double>(M) * K + static_cast<double>(K) * N +
                               static_cast<double>(M) * N);
-  *splits_out = r.splits;
   return std::max(us, bytes / kHbmBytesPerUs + c.fixed_us);
 }
 
-void plan(int M, int N, int K, int *kernel, int *split, const Problem *general = nullptr) {
-  *kernel = kPlanCandidates[0].kernel;
-  *split = 1;
+struct PlanChoice {
+  int kernel;
+  int split;
+  bool tail;   // split only the last, partial round of tiles
+};
+
+PlanChoice plan(int M, int N, int K, const Problem *general = nullptr) {
+  PlanChoice best_plan{kPlanCandidates[0].kernel, 1, false};
   double best = 1e30;
   Problem pr = general ? *general : plain_problem(nullptr, nullptr, nullptr, M, N, K);
   pr.K = K;
@@ -199,17 +235,22 @@ void plan(int M, int N, int K, int *kernel, int *split, const Problem *general =
     }
     for (int s = 1; s <= 64; s *= 2) {
       if (s > 1 && K / s < 256) break;   // each K range keeps >= 256 elements
-      int launched = s;
-      const double us = plan_cost_us(pr, c, s, &launched);
-      if (launched < s) break;           // fewer K steps than ranges asked for
-      // Ties (within 1%) go to the candidate seen first: bigger tiles, fewer splits.
-      if (us < best * 0.99) {
-        best = us;
-        *kernel = c.kernel;
-        *split = s;
+      for (int tail = 0; tail <= (s > 1 ? 1 : 0); ++tail) {
+        Resolved r;
+        const double us = plan_cost_us(pr, c, s, tail != 0, &r);
+        if (us >= 1e30) continue;
+        if (r.splits < s) break;                // fewer K steps than ranges asked for
+        if (tail && r.dp_tiles == 0) continue;  // the same as splitting every tile
+        // Ties (within 1%) go to the plan seen first: bigger tiles, fewer
+        // splits, every tile split before a split tail.
+        if (us < best * 0.99) {
+          best = us;
+          best_plan = PlanChoice{c.kernel, s, tail != 0};
+        }
       }
     }
   }
+  return best_plan;
 }
 
 // ---------------------------------------------------------------------------
@@ -306,31 +347,31 @@ bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K
 
 // Kernels fed by direct global -> LDS copies (16-byte copies from 4-byte
 // aligned sources, any K, N and row strides, either storage order of each
-// operand). Writes alpha * op(A) op(B) + beta * out (row stride ldo) for the
-// tile's K range. Returns false (nothing launched) when the operand offsets
-// of one workgroup would not fit in 32 bits.
+// operand). Whole tiles get alpha * op(A) op(B) + beta * C, split ones their
+// K range's partial product in workspace slab s (ws + s * slab, row stride
+// N). Returns false (nothing launched) when the operand offsets of one
+// workgroup would not fit in 32 bits.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE, bool A_KM,
           bool B_KM>
-void launch_dma_t(const Problem &p, float *out, int ldo, float alpha, float beta,
-                  const Resolved &r, long long slab, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
+void launch_dma_t(const Problem &p, float *ws, const Resolved &r, long long slab,
+                  hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(r.workgroups()));
   hipLaunchKernelGGL(
       (gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE, A_KM, B_KM>), grid,
-      dim3(64 * WAVES_M * WAVES_N), 0, stream, p.A, p.B, out, p.M, p.N, p.K, p.lda, p.ldb, ldo,
-      alpha, beta, r.k_chunk, static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits,
-      slab);
+      dim3(64 * WAVES_M * WAVES_N), 0, stream, p.A, p.B, p.C, ws, p.M, p.N, p.K, p.lda, p.ldb,
+      p.ldc, p.alpha, p.beta, r.k_chunk, static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n),
+      r.splits, static_cast<int>(r.dp_tiles), slab);
 }
 
 // ALL_ORDERS: the configuration is built for transposed operands too (the
 // planner's three); the others take op(A) = A, op(B) = B only.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE,
           bool ALL_ORDERS>
-bool launch_dma(const Problem &p, float *out, int ldo, float alpha, float beta,
-                const Resolved &r, long long slab, hipStream_t stream) {
-  if (!dma_fits(p, BM, BN, BK, r.k_chunk)) return false;
-#define LGEMM_DMA(AK, BKM)                                                                    \
-  launch_dma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, WPE, AK, BKM>(p, out, ldo, alpha, beta, r, \
-                                                                  slab, stream)
+bool launch_dma(const Problem &p, float *ws, const Resolved &r, long long slab,
+                hipStream_t stream) {
+  if (!dma_fits(p, BM, BN, BK, r.k_span())) return false;
+#define LGEMM_DMA(AK, BKM)                                                                  \
+  launch_dma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, WPE, AK, BKM>(p, ws, r, slab, stream)
   if (!p.ta && !p.tb) {
     LGEMM_DMA(true, false);
     return true;
@@ -345,20 +386,24 @@ bool launch_dma(const Problem &p, float *out, int ldo, float alpha, float beta,
   return false;
 }
 
-// Launch the kernel of r.k, writing alpha * op(A) op(B) + beta * out (row
-// stride ldo). Register-staged, vector-FMA and ladder kernels take the plain
-// problem only (op = identity, dense, ldo = N, alpha = 1, beta = 0); a
-// copy-fed kernel whose offsets would not fit runs the register-staged kernel
-// of its tile for a plain problem. Returns false if nothing could be launched.
-bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, float beta,
-                        const Resolved &r, long long slab, hipStream_t stream) {
+// Launch the kernel of r.k for the product or, when r splits K, the partial
+// products into the workspace (slabs of M x N). Register-staged, vector-FMA
+// and ladder kernels write `out` (C, or the workspace when split) with row
+// stride N and take the plain problem only (op = identity, dense operands;
+// alpha = 1, beta = 0, ldc = N unless split) and no split tail; a copy-fed
+// kernel whose offsets would not fit runs the register-staged kernel of its
+// tile for such a problem. Returns false if nothing could be launched.
+bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
+                        hipStream_t stream) {
   const float *A = p.A, *B = p.B;
   const int M = p.M, N = p.N, K = p.K;
-  const bool plain = !p.ta && !p.tb && p.lda == K && p.ldb == N && ldo == N && alpha == 1.0f &&
-                     beta == 0.0f;
-  const bool dma_kernel = (r.k->id >= GEMM_KERNEL_DMA32_256x256_W8 &&
-                           r.k->id <= GEMM_KERNEL_DMA32_128x128_W8) ||
-                          r.k->id == GEMM_KERNEL_DMA32_64x64_S3;
+  const bool split = r.splits > 1;
+  float *ws = static_cast<float *>(workspace);
+  float *out = split ? ws : p.C;
+  const long long slab = split ? (long long)M * N : 0;
+  const bool plain = !p.ta && !p.tb && p.lda == K && p.ldb == N && r.dp_tiles == 0 &&
+                     (split || (p.ldc == N && p.alpha == 1.0f && p.beta == 0.0f));
+  const bool dma_kernel = is_dma_kernel(r.k->id);
   if (!plain && !dma_kernel) return false;
   switch (r.k->id) {
     case GEMM_KERNEL_MFMA_256x256:
@@ -399,48 +444,39 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
       launch_mfma<32, 64, 64, 16, 1, 1, 2, true>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_DMA32_256x256_W8:
-      return launch_dma<32, 256, 256, 16, 2, 4, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                             stream) ||
+      return launch_dma<32, 256, 256, 16, 2, 4, 4, 2, false>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
-      return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, out, ldo, alpha, beta, r, slab,
-                                                            stream) ||
+      return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_128x128_W4:
-      return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                            stream) ||
+      return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA16_128x128_W4:
-      return launch_dma<16, 128, 128, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                             stream) ||
+      return launch_dma<16, 128, 128, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA16_64x64:
-      return launch_dma<16, 64, 64, 32, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                           stream) ||
+      return launch_dma<16, 64, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA32_64x64:
-      return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                          stream) ||
+      return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA16_128x64:
-      return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, out, ldo, alpha, beta, r, slab,
-                                                            stream) ||
+      return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA32_128x128_W8:
-      return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, true>(p, out, ldo, alpha, beta, r, slab,
-                                                            stream) ||
+      return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, true>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_64x64_S3:
-      return launch_dma<32, 64, 64, 16, 2, 2, 3, 2, true>(p, out, ldo, alpha, beta, r, slab,
-                                                           stream) ||
+      return launch_dma<32, 64, 64, 16, 2, 2, 3, 2, true>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_VALU_64x64: {
@@ -474,25 +510,37 @@ bool launch_gemm_kernel(const Problem &p, float *out, int ldo, float alpha, floa
 }
 
 // One pass of the product with a resolved plan: the kernel, then (split K)
-// the reduction of the partial slabs into C with alpha and beta.
+// the reduction of the partial slabs into C with alpha and beta, over all of
+// C or (split tail) over the split tiles only.
 int launch(const Problem &p, const Resolved &r, void *workspace, hipStream_t stream) {
-  const bool split = r.splits > 1;
-  float *out = split ? static_cast<float *>(workspace) : p.C;
-  const long long slab = split ? (long long)p.M * p.N : 0;
-  if (!launch_gemm_kernel(p, out, split ? p.N : p.ldc, split ? 1.0f : p.alpha,
-                          split ? 0.0f : p.beta, r, slab, stream))
-    return GEMM_ERR_INVALID_PLAN;
+  if (!launch_gemm_kernel(p, workspace, r, stream)) return GEMM_ERR_INVALID_PLAN;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
-  if (split) {
+  if (r.splits > 1) {
     const long long count = (long long)p.M * p.N;
     const bool v4 = (p.N % 4 == 0) && (p.ldc % 4 == 0) &&
                     (reinterpret_cast<uintptr_t>(p.C) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(workspace) % 16 == 0);
+    const float *ws = static_cast<const float *>(workspace);
+    if (r.dp_tiles > 0) {
+      const int bm = r.k->bm, bn = r.k->bn;
+      const long long per_tile = (long long)bm * (v4 ? bn / 4 : bn);
+      const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n - r.dp_tiles),
+                      static_cast<unsigned>(ceil_div(per_tile, 4 * gemm::kThreads)));
+      const int tm = static_cast<int>(r.tiles_m), tn = static_cast<int>(r.tiles_n);
+      const int dp = static_cast<int>(r.dp_tiles);
+      if (v4)
+        hipLaunchKernelGGL(gemm::tail_reduce_kernel<4>, grid, dim3(gemm::kThreads), 0, stream, ws,
+                           p.C, p.M, p.N, p.ldc, tm, tn, dp, bm, bn, r.splits, p.alpha, p.beta);
+      else
+        hipLaunchKernelGGL(gemm::tail_reduce_kernel<1>, grid, dim3(gemm::kThreads), 0, stream, ws,
+                           p.C, p.M, p.N, p.ldc, tm, tn, dp, bm, bn, r.splits, p.alpha, p.beta);
+      e = hipGetLastError();
+      return e == hipSuccess ? GEMM_OK : hip_fail(e);
+    }
     const long long items = v4 ? count / 4 : count;
     const unsigned blocks =
         static_cast<unsigned>(std::min<long long>(ceil_div(items, gemm::kThreads), 4 * kNumCus));
-    const float *ws = static_cast<const float *>(workspace);
     if (v4)
       hipLaunchKernelGGL(gemm::splitk_reduce_kernel<4>, dim3(blocks), dim3(gemm::kThreads), 0,
                          stream, ws, p.C, count, p.N, p.ldc, r.splits, p.alpha, p.beta);
@@ -549,16 +597,17 @@ int run(const float *A, const float *B, float *C, int M, int N, int K, const gem
         void *workspace, size_t workspace_bytes, bool own_ws, hipStream_t stream) {
   int st = validate(A, B, C, M, N, K);
   if (st != GEMM_OK) return st;
-  int kernel = GEMM_KERNEL_AUTO, split = 1;
+  PlanChoice pc{GEMM_KERNEL_AUTO, 1, false};
   if (plan_in) {
-    kernel = plan_in->kernel;
-    split = plan_in->split_k;
-    if (kernel != GEMM_KERNEL_AUTO && (!find_kernel(kernel) || split < 1))
+    pc = PlanChoice{plan_in->kernel, plan_in->split_k, plan_in->split_tail != 0};
+    if (pc.kernel != GEMM_KERNEL_AUTO &&
+        (!find_kernel(pc.kernel) || pc.split < 1 || plan_in->split_tail < 0 ||
+         plan_in->split_tail > 1))
       return GEMM_ERR_INVALID_PLAN;
   }
-  if (kernel == GEMM_KERNEL_AUTO) plan(M, N, K, &kernel, &split);
+  if (pc.kernel == GEMM_KERNEL_AUTO) pc = plan(M, N, K);
   Resolved r;
-  if (!resolve(M, N, K, kernel, split, &r)) return GEMM_ERR_INVALID_PLAN;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return GEMM_ERR_INVALID_PLAN;
   const size_t need = workspace_for(M, N, r);
   if (!own_ws && need > 0 && (workspace == nullptr || workspace_bytes < need))
     return GEMM_ERR_WORKSPACE;
@@ -574,7 +623,7 @@ int run(const float *A, const float *B, float *C, int M, int N, int K, const gem
     workspace = library_workspace(dev, need, &st);
     if (st != GEMM_OK) return st;
     // No workspace available: same kernel without the split.
-    if (!workspace && !resolve(M, N, K, kernel, 1, &r)) return GEMM_ERR_INVALID_PLAN;
+    if (!workspace && !resolve(M, N, K, pc.kernel, 1, false, &r)) return GEMM_ERR_INVALID_PLAN;
   }
   return launch(p, r, workspace, stream);
 }
@@ -607,11 +656,11 @@ int validate_general(const Problem &p) {
 // would not fit in 32 bits, K is cut into passes of *k_pass elements, run
 // one after the other (the second and later with beta = 1), and the plan is
 // made for one pass.
-bool plan_general(const Problem &p, int *kernel, int *split, int *k_pass) {
+bool plan_general(const Problem &p, PlanChoice *pc, int *k_pass) {
   long long k_eff = std::max(p.K, 1);
   for (int iter = 0; iter < 8; ++iter) {
-    plan(p.M, p.N, static_cast<int>(k_eff), kernel, split, &p);
-    const KernelInfo *k = find_kernel(*kernel);
+    *pc = plan(p.M, p.N, static_cast<int>(k_eff), &p);
+    const KernelInfo *k = find_kernel(pc->kernel);
     if (!dma_tile_usable(p, k->bm, k->bn, k->bk)) return false;
     auto fits = [&](long long kc) {
       const long long span = ceil_div(kc, k->bk) * k->bk + k->bk;
@@ -631,12 +680,12 @@ bool plan_general(const Problem &p, int *kernel, int *split, int *k_pass) {
 
 // Workspace of the general form: the largest of its passes' (the last pass
 // may be shorter and split differently).
-size_t general_workspace(const Problem &p, int kernel, int split, int k_pass) {
+size_t general_workspace(const Problem &p, const PlanChoice &pc, int k_pass) {
   size_t need = 0;
   const int lens[2] = {std::min(k_pass, p.K), p.K > k_pass ? p.K % k_pass : 0};
   for (int len : lens) {
     Resolved r;
-    if (len > 0 && resolve(p.M, p.N, len, kernel, split, &r))
+    if (len > 0 && resolve(p.M, p.N, len, pc.kernel, pc.split, pc.tail, &r))
       need = std::max(need, workspace_for(p.M, p.N, r));
   }
   return need;
@@ -646,10 +695,11 @@ int run_general(Problem p, void *workspace, size_t workspace_bytes, hipStream_t 
   int st = validate_general(p);
   if (st != GEMM_OK) return st;
   if (p.M == 0 || p.N == 0) return GEMM_OK;
-  int kernel = 0, split = 1, k_pass = std::max(p.K, 1);
+  PlanChoice pc{0, 1, false};
+  int k_pass = std::max(p.K, 1);
   const bool uses_ab = p.K > 0 && p.alpha != 0.0f;
-  if (uses_ab && !plan_general(p, &kernel, &split, &k_pass)) return GEMM_ERR_INVALID_DIM;
-  const size_t need = uses_ab ? general_workspace(p, kernel, split, k_pass) : 0;
+  if (uses_ab && !plan_general(p, &pc, &k_pass)) return GEMM_ERR_INVALID_DIM;
+  const size_t need = uses_ab ? general_workspace(p, pc, k_pass) : 0;
   const bool own_ws = workspace == nullptr;
   if (!own_ws && workspace_bytes < need) return GEMM_ERR_WORKSPACE;
 
@@ -660,7 +710,7 @@ int run_general(Problem p, void *workspace, size_t workspace_bytes, hipStream_t 
   if (own_ws && need > 0) {
     workspace = library_workspace(dev, need, &st);
     if (st != GEMM_OK) return st;
-    if (!workspace) split = 1;   // no workspace available: no split
+    if (!workspace) pc.split = 1;   // no workspace available: no split
   }
   // K passes: op(A)[:, k0:k0+kp] op(B)[k0:k0+kp, :], accumulated into C.
   const float beta0 = p.beta;
@@ -671,7 +721,7 @@ int run_general(Problem p, void *workspace, size_t workspace_bytes, hipStream_t 
     q.B = p.B + (p.tb ? k0 : (long long)k0 * p.ldb);
     q.beta = k0 == 0 ? beta0 : 1.0f;
     Resolved r;
-    if (!resolve(q.M, q.N, q.K, kernel, split, &r)) return GEMM_ERR_INVALID_PLAN;
+    if (!resolve(q.M, q.N, q.K, pc.kernel, pc.split, pc.tail, &r)) return GEMM_ERR_INVALID_PLAN;
     st = launch(q, r, workspace, stream);
     if (st != GEMM_OK) return st;
   }
@@ -688,10 +738,9 @@ int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K, hipS
 
 size_t gemm_f32_workspace_bytes(int M, int N, int K) {
   if (M < 0 || N < 0 || K < 0) return 0;
-  int kernel, split;
-  plan(M, N, K, &kernel, &split);
+  const PlanChoice pc = plan(M, N, K);
   Resolved r;
-  if (!resolve(M, N, K, kernel, split, &r)) return 0;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return 0;
   return workspace_for(M, N, r);
 }
 
@@ -703,23 +752,23 @@ int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K, v
 int gemm_f32_plan(int M, int N, int K, gemm_plan_t *out) {
   if (!out) return GEMM_ERR_NULL_PTR;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_DIM;
-  int kernel, split;
-  plan(M, N, K, &kernel, &split);
+  const PlanChoice pc = plan(M, N, K);
   Resolved r;
-  if (!resolve(M, N, K, kernel, split, &r)) return GEMM_ERR_INVALID_PLAN;
-  out->kernel = kernel;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return GEMM_ERR_INVALID_PLAN;
+  out->kernel = pc.kernel;
   out->split_k = r.splits;
   out->k_chunk = r.k_chunk;
-  out->reserved = 0;
+  out->split_tail = r.dp_tiles > 0 ? 1 : 0;
   return GEMM_OK;
 }
 
 size_t gemm_f32_plan_workspace_bytes(int M, int N, int K, const gemm_plan_t *p) {
   if (!p || M < 0 || N < 0 || K < 0) return 0;
-  int kernel = p->kernel, split = p->split_k;
-  if (kernel == GEMM_KERNEL_AUTO) plan(M, N, K, &kernel, &split);
+  PlanChoice pc{p->kernel, p->split_k, p->split_tail != 0};
+  if (pc.kernel == GEMM_KERNEL_AUTO) pc = plan(M, N, K);
+  else if (p->split_tail < 0 || p->split_tail > 1) return 0;
   Resolved r;
-  if (!resolve(M, N, K, kernel, split, &r)) return 0;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return 0;
   return workspace_for(M, N, r);
 }
 
@@ -746,9 +795,10 @@ size_t gemm_f32_general_workspace_bytes(int trans_a, int trans_b, int M, int N, 
   const int a_cols = p.ta ? M : K, b_cols = p.tb ? K : N;
   if (lda < std::max(1, a_cols) || ldb < std::max(1, b_cols)) return 0;
   if (M == 0 || N == 0 || K == 0) return 0;
-  int kernel = 0, split = 1, k_pass = K;
-  if (!plan_general(p, &kernel, &split, &k_pass)) return 0;
-  return general_workspace(p, kernel, split, k_pass);
+  PlanChoice pc{0, 1, false};
+  int k_pass = K;
+  if (!plan_general(p, &pc, &k_pass)) return 0;
+  return general_workspace(p, pc, k_pass);
 }
 
 const char *gemm_kernel_name(int kernel) {

@@ -33,37 +33,61 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;  // 4 waves of 64 lanes per workgroup
 constexpr int kXcds = 8;       // MI355X: 8 accelerator dies of 32 CUs each
 
+constexpr int kGroupM = 8;     // tile rows per group of the tile order
+
 struct TileCoord {
   int tm, tn, split;
+  int whole;   // 1: the tile's whole K range, stored into C
 };
 
-// Workgroup id -> (tile row, tile column, K range).
-//
 // The dispatcher hands consecutive workgroup ids to the 8 XCDs round robin,
-// and each XCD has its own L2. The first step renumbers ids so that each XCD
-// receives one contiguous range of logical ids (a bijection for any count).
-// Logical ids then run over K ranges slowest, and within one K range over
-// tiles in groups of `group_m` tile rows, column by column inside a group, so
-// that the workgroups resident on one XCD at one time share A row panels and
-// B column panels in that XCD's L2.
-__device__ inline TileCoord map_tile(int bid, int tiles_m, int tiles_n, int splits,
-                                     int group_m) {
-  const int total = tiles_m * tiles_n * splits;
+// and each XCD has its own L2. This renumbering of ids 0 .. total-1 gives
+// each XCD one contiguous range of logical ids (a bijection for any count).
+__device__ inline int xcd_order(int bid, int total) {
   const int q = total / kXcds, r = total % kXcds;
   const int xcd = bid % kXcds, local = bid / kXcds;
-  const int id = xcd * q + (xcd < r ? xcd : r) + local;
-  const int tiles = tiles_m * tiles_n;
-  TileCoord c;
-  c.split = id / tiles;
-  const int t = id - c.split * tiles;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+// Tile order: tiles in groups of `group_m` tile rows, column by column inside
+// a group, so that the workgroups resident on one XCD at one time share A row
+// panels and B column panels in that XCD's L2. Tile t -> (tile row, column).
+__device__ inline void grouped_tile(int t, int tiles_m, int tiles_n, int group_m, int *tm,
+                                    int *tn) {
   const int per_group = group_m * tiles_n;
   const int g = t / per_group;
   const int first_m = g * group_m;
   const int rows_left = tiles_m - first_m;
   const int gsize = rows_left < group_m ? rows_left : group_m;
   const int within = t - g * per_group;
-  c.tm = first_m + within % gsize;
-  c.tn = within / gsize;
+  *tm = first_m + within % gsize;
+  *tn = within / gsize;
+}
+
+// Workgroup id -> (tile row, tile column, K range).
+//
+// The first `dp_tiles` tiles of the tile order are computed whole, one
+// workgroup each (ids 0 .. dp_tiles-1); every later tile is cut into `splits`
+// K ranges, one workgroup each (the ids after). With dp_tiles = 0 every tile
+// is split (plain split-K; splits = 1: one workgroup per tile). Within each
+// of the two id ranges ids are renumbered per XCD (xcd_order), and the split
+// part runs over K ranges slowest.
+__device__ inline TileCoord map_tile(int bid, int tiles_m, int tiles_n, int splits, int group_m,
+                                     int dp_tiles = 0) {
+  TileCoord c;
+  int t;
+  if (bid < dp_tiles) {
+    t = xcd_order(bid, dp_tiles);
+    c.split = 0;
+    c.whole = 1;
+  } else {
+    const int tail = tiles_m * tiles_n - dp_tiles;
+    const int id = xcd_order(bid - dp_tiles, tail * splits);
+    c.split = id / tail;
+    t = dp_tiles + (id - c.split * tail);
+    c.whole = splits == 1;
+  }
+  grouped_tile(t, tiles_m, tiles_n, group_m, &c.tm, &c.tn);
   return c;
 }
 
@@ -177,7 +201,7 @@ void mfma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
   __shared__ __attribute__((aligned(16))) float As[2][BM * LDA];
   __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
 
-  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, 8);
+  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, kGroupM);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
   const int k_begin = tc.split * k_chunk;
   const int k_end = min(K, k_begin + k_chunk);
@@ -613,20 +637,20 @@ struct DmaShape {
   static_assert(NG % 2 == 0 || NS % 2 == 0, "fragment slots repeat with the stage ring");
 };
 
-// C <- alpha * op(A) op(B) + beta * C for one output tile (or, with split-K,
-// the partial product of one K range into workspace slab `split`, with
-// alpha = 1, beta = 0 and ldc = N). op(A) is K-contiguous when A_KMAJOR (A
-// given M x K), op(B) when B_KMAJOR (B given N x K, i.e. transposed).
-// beta == 0: C is not read.
+// C <- alpha * op(A) op(B) + beta * C for one output tile (row stride ldc),
+// or, for a tile that map_tile splits, the partial product of one K range
+// into workspace slab `split` (ws + split * slab, row stride N, written as
+// is). op(A) is K-contiguous when A_KMAJOR (A given M x K), op(B) when
+// B_KMAJOR (B given N x K, i.e. transposed). beta == 0: C is not read.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC,
           int WAVES_PER_EU, bool A_KMAJOR, bool B_KMAJOR>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
-                          float *__restrict__ C, int M, int N, int K, int lda, int ldb, int ldc,
-                          float alpha, float beta, int k_chunk, int tiles_m, int tiles_n,
-                          int splits, long long slab) {
+                          float *__restrict__ C, float *__restrict__ ws, int M, int N, int K,
+                          int lda, int ldb, int ldc, float alpha, float beta, int k_chunk,
+                          int tiles_m, int tiles_n, int splits, int dp_tiles, long long slab) {
   using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, VEC, A_KMAJOR, B_KMAJOR>;
   using OpA = typename S::OpA;
   using OpB = typename S::OpB;
@@ -644,14 +668,19 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // which otherwise keeps the results of the integer divisions of map_tile
   // in vector registers and everything derived from them (the buffer
   // resources, the copy bases) with them.
-  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, 8);
+  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, kGroupM, dp_tiles);
   const int m0 = __builtin_amdgcn_readfirstlane(tc.tm) * BM;
   const int n0 = __builtin_amdgcn_readfirstlane(tc.tn) * BN;
   const int split = __builtin_amdgcn_readfirstlane(tc.split);
-  const int k_begin = split * k_chunk;
-  const int k_end = min(K, k_begin + k_chunk);
+  const bool whole = __builtin_amdgcn_readfirstlane(tc.whole) != 0;
+  const int k_begin = whole ? 0 : split * k_chunk;
+  const int k_end = whole ? K : min(K, k_begin + k_chunk);
   const int nk = (k_end - k_begin + BK - 1) / BK;
-  float *__restrict__ Cout = C + (long long)split * slab;
+  // Output of this workgroup: C, or its K range's workspace slab.
+  float *__restrict__ Cout = whole ? C : ws + (long long)split * slab;
+  const int ldo = whole ? ldc : N;
+  const float alpha_o = whole ? alpha : 1.0f;
+  const float beta_o = whole ? beta : 0.0f;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -894,7 +923,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
           for (int v = 0; v < S::ACC; ++v) {
             const int row = m0 + wm * S::WM + OpA::x_of(fm, Op::row(q, v));
             const bool in = !kChecked || (row < M && col < N);
-            cv[fn][v] = in ? Cout[(long long)row * ldc + col] : 0.0f;
+            cv[fn][v] = in ? Cout[(long long)row * ldo + col] : 0.0f;
           }
         }
       }
@@ -905,18 +934,18 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         for (int v = 0; v < S::ACC; ++v) {
           const int row = m0 + wm * S::WM + OpA::x_of(fm, Op::row(q, v));
           if (!kChecked || (row < M && col < N)) {
-            float *p = Cout + (long long)row * ldc + col;
+            float *p = Cout + (long long)row * ldo + col;
             if constexpr (kBetaZero)
-              *p = alpha * acc[fm][fn][v];
+              *p = alpha_o * acc[fm][fn][v];
             else
-              *p = __builtin_fmaf(alpha, acc[fm][fn][v], beta * cv[fn][v]);
+              *p = __builtin_fmaf(alpha_o, acc[fm][fn][v], beta_o * cv[fn][v]);
           }
         }
       }
     }
   };
   const bool interior = m0 + BM <= M && n0 + BN <= N;
-  if (beta == 0.0f) {
+  if (beta_o == 0.0f) {
     if (interior) store_tile(std::true_type(), std::false_type());
     else store_tile(std::true_type(), std::true_type());
   } else {
@@ -941,7 +970,7 @@ void valu_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
   __shared__ __attribute__((aligned(16))) float At[BK * LD];
   __shared__ __attribute__((aligned(16))) float Bs[BK * LD];
 
-  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, 8);
+  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, kGroupM);
   const int m0 = tc.tm * BM, n0 = tc.tn * BN;
   const int k_begin = tc.split * k_chunk;
   const int k_end = min(K, k_begin + k_chunk);
@@ -1026,6 +1055,54 @@ void splitk_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, l
     } else {
       float s = ws[first];
       for (int p = 1; p < splits; ++p) s = s + ws[(long long)p * count + first];
+      *out = beta == 0.0f ? alpha * s : __builtin_fmaf(alpha, s, beta * *out);
+    }
+  }
+}
+
+// Reduction of a split tail: for each tile after the first dp_tiles of the
+// tile order (map_tile), C <- alpha * sum_s ws[s] + beta * C over its
+// elements inside C, the slabs summed in ascending order as above. The slabs
+// are M x N with row stride N; only these tiles' elements are read. Grid:
+// x = tail tile, y = parts of one tile. V = 4 as above (N and ldc multiples
+// of 4, 16-byte aligned: a tile's row segment is then whole float4s).
+template <int V>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
+void tail_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, int M, int N, int ldc,
+                        int tiles_m, int tiles_n, int dp_tiles, int bm, int bn, int splits,
+                        float alpha, float beta) {
+  int tm, tn;
+  grouped_tile(dp_tiles + blockIdx.x, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  const int m0 = tm * bm, n0 = tn * bn;
+  const int rows = min(bm, M - m0), cols = min(bn, N - n0);
+  const int per_row = (cols + V - 1) / V;
+  const int items = rows * per_row;
+  const long long slab = (long long)M * N;
+  for (int e = blockIdx.y * kThreads + threadIdx.x; e < items; e += gridDim.y * kThreads) {
+    const int r = e / per_row;
+    const int c = (e - r * per_row) * V;
+    const long long w = (long long)(m0 + r) * N + n0 + c;
+    float *out = C + (long long)(m0 + r) * ldc + n0 + c;
+    if constexpr (V == 4) {
+      floatx4 s = *reinterpret_cast<const floatx4 *>(ws + w);
+      for (int p = 1; p < splits; ++p) {
+        const floatx4 v = *reinterpret_cast<const floatx4 *>(ws + (long long)p * slab + w);
+        s[0] = s[0] + v[0]; s[1] = s[1] + v[1]; s[2] = s[2] + v[2]; s[3] = s[3] + v[3];
+      }
+      floatx4 o;
+      if (beta == 0.0f) {
+        o[0] = alpha * s[0]; o[1] = alpha * s[1]; o[2] = alpha * s[2]; o[3] = alpha * s[3];
+      } else {
+        const floatx4 cv = *reinterpret_cast<const floatx4 *>(out);
+        o[0] = __builtin_fmaf(alpha, s[0], beta * cv[0]);
+        o[1] = __builtin_fmaf(alpha, s[1], beta * cv[1]);
+        o[2] = __builtin_fmaf(alpha, s[2], beta * cv[2]);
+        o[3] = __builtin_fmaf(alpha, s[3], beta * cv[3]);
+      }
+      *reinterpret_cast<floatx4 *>(out) = o;
+    } else {
+      float s = ws[w];
+      for (int p = 1; p < splits; ++p) s = s + ws[(long long)p * slab + w];
       *out = beta == 0.0f ? alpha * s : __builtin_fmaf(alpha, s, beta * *out);
     }
   }

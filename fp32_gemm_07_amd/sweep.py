@@ -8,7 +8,9 @@ For each shape: the planner's choice, torch.matmul in FP32 (the vendor
 library, for context), and the four fastest (kernel, split) plans, each the
 median of HIP-event timings of back-to-back launches on inputs resident on
 the GPU (uniform [-1, 1) values; timing only, nothing is checked). This is
-the measurement the planner's cost model is fitted to.
+the measurement the planner's cost model is fitted to. "S4" splits every
+tile into 4 K ranges; "S4t" only the tiles of the last, partial round of
+256 (the planner's kernels, shapes with such a round).
 
 --ladder times the optimisation ladder of the yekq.top LeetGPU walkthrough
 (v0 .. v4, then the matrix-core kernels) on its two shapes, 1024 x 512 x 1024
@@ -36,6 +38,11 @@ KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4", "dma32
            "mfma32_64x64", "valu_64x64"]
 SPLITS = (1, 2, 4, 8, 16, 32, 64)
 MAX_WORKSPACE = 2 << 30
+TAIL_KERNELS = {"dma32_256x256_w8_s3": 256, "dma32_128x128_w8": 128, "dma32_64x64_s3": 64}
+
+
+def plan_label(plan) -> str:
+    return f"S{plan.split_k}" + ("t" if plan.split_tail else "")
 
 
 LADDER_SHAPES = ["1024x512x1024", "1001x513x777"]
@@ -188,17 +195,24 @@ def main(argv=None) -> int:
             for sp in SPLITS:
                 if sp > 1 and K // sp < 256:
                     continue
-                plan = binding.make_plan(binding.KERNELS[kn], sp)
-                if binding.gemm_f32_plan_workspace_bytes(M, N, K, plan) > MAX_WORKSPACE:
-                    continue
-                res.append((timeit(plan_call(plan)), f"{kn}/S{sp}"))
+                tails = [False]
+                if sp > 1 and kn in TAIL_KERNELS:
+                    t = TAIL_KERNELS[kn]
+                    tiles = -(-M // t) * -(-N // t)
+                    if tiles > 256 and tiles % 256:
+                        tails.append(True)
+                for tail in tails:
+                    plan = binding.make_plan(binding.KERNELS[kn], sp, tail)
+                    if binding.gemm_f32_plan_workspace_bytes(M, N, K, plan) > MAX_WORKSPACE:
+                        continue
+                    res.append((timeit(plan_call(plan)), f"{kn}/{plan_label(plan)}"))
         auto = binding.gemm_f32_plan(M, N, K)
         t_auto = timeit(plan_call(auto))
         torch.backends.cuda.matmul.allow_tf32 = False
         t_vendor = timeit(lambda: torch.matmul(dA, dB, out=dC))
         res.sort()
         top = "  ".join(f"{name} {us:.1f}" for us, name in res[:4])
-        print(f"{M}x{K}x{N}: auto {binding.gemm_kernel_name(auto.kernel)}/S{auto.split_k} "
+        print(f"{M}x{K}x{N}: auto {binding.gemm_kernel_name(auto.kernel)}/{plan_label(auto)} "
               f"{t_auto:.1f} us ({flop / t_auto / 1e6:.1f} TF) | vendor {t_vendor:.1f} us "
               f"({flop / t_vendor / 1e6:.1f} TF) | best {top}", flush=True)
     return 0

@@ -15,7 +15,8 @@
  * nothing. The sum is evaluated in FP32 (FP32 MFMA products and accumulation;
  * with split-K, S partial sums over contiguous K ranges are added in
  * ascending range order), so results are reproducible run to run for a given
- * plan but are not in general bit-identical to a sequential sum.
+ * plan but are not in general bit-identical to a sequential sum. Whether a
+ * given output is split depends on the plan alone (never on timing).
  *
  * Calling convention shared by every entry point:
  *   - Pointers are device pointers on the current HIP device; `stream` is a
@@ -53,7 +54,7 @@ enum {
                                     (A, B when M, N, K > 0; C when M, N > 0) */
   GEMM_ERR_ALIAS = 3,            /* C overlaps A or B */
   GEMM_ERR_WORKSPACE = 4,        /* workspace missing or smaller than required */
-  GEMM_ERR_INVALID_PLAN = 5,     /* unknown kernel id or split count < 1 */
+  GEMM_ERR_INVALID_PLAN = 5,     /* unknown kernel id, split count < 1 or unusable split_tail */
   GEMM_ERR_HIP = 6,              /* a HIP call failed; see gemm_last_hip_error() */
   GEMM_ERR_UNSUPPORTED_DEVICE = 7 /* the current device is not gfx950 */
 };
@@ -99,12 +100,20 @@ enum {
 
 /* An execution plan: which kernel, and how many contiguous K ranges
  * ("split-K") the contraction is cut into. k_chunk is the length of each
- * range (a multiple of the kernel's K step); split_k = ceil(K / k_chunk). */
+ * range (a multiple of the kernel's K step); split_k = ceil(K / k_chunk).
+ *
+ * split_tail = 0: every output tile is split into split_k K ranges.
+ * split_tail = 1 (copy-fed kernels, ids 30-39 and 45, only): the output tiles
+ * are taken in rounds of 256 (one per CU); the tiles of the whole rounds are
+ * computed over all of K and stored straight into C, and only the tiles of
+ * the last, partial round are split into split_k K ranges, so that the last
+ * round's work is spread over all CUs. With fewer than 256 tiles this is the
+ * same as split_tail = 0; with a multiple of 256 tiles nothing is split. */
 typedef struct gemm_plan {
   int kernel;
   int split_k;
   int k_chunk;
-  int reserved;
+  int split_tail;
 } gemm_plan_t;
 
 /* C = A x B with the planner's choice of kernel and split. When that plan
@@ -116,7 +125,9 @@ int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K,
              hipStream_t stream);
 
 /* Bytes of workspace the planner's plan for (M, N, K) needs:
- * 4 * split_k * M * N when it splits K, else 0. Returns 0 for invalid dims. */
+ * 4 * split_k * M * N when it splits K (one M x N slab per K range, also
+ * when only the last round of tiles is split), else 0. Returns 0 for invalid
+ * dims. */
 size_t gemm_f32_workspace_bytes(int M, int N, int K);
 
 /* As gemm_f32, with a caller-owned device workspace of workspace_bytes bytes
@@ -130,12 +141,15 @@ int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K,
 int gemm_f32_plan(int M, int N, int K, gemm_plan_t *plan);
 
 /* Workspace bytes an explicit plan needs (0 for an invalid plan or dims). Only
- * plan->kernel and plan->split_k are read. */
+ * plan->kernel, plan->split_k and plan->split_tail are read. */
 size_t gemm_f32_plan_workspace_bytes(int M, int N, int K, const gemm_plan_t *plan);
 
-/* C = A x B with an explicit plan (plan->kernel, plan->split_k; split_k is
- * clamped to the number of K steps). kernel = GEMM_KERNEL_AUTO means the
- * planner's choice. workspace as for gemm_f32_ex. Returns a status code. */
+/* C = A x B with an explicit plan (plan->kernel, plan->split_k,
+ * plan->split_tail; split_k is clamped to the number of K steps).
+ * kernel = GEMM_KERNEL_AUTO means the planner's choice. workspace as for
+ * gemm_f32_ex. GEMM_ERR_INVALID_PLAN for split_tail other than 0 or 1, or 1
+ * with a kernel that is not copy-fed or whose copy offsets would not fit
+ * for this shape. Returns a status code. */
 int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, int K,
                        const gemm_plan_t *plan, void *workspace, size_t workspace_bytes,
                        hipStream_t stream);

@@ -116,6 +116,33 @@ def test_planner_choices_for_standing_workloads():
         assert binding.gemm_kernel_name(p.kernel) != "unknown"
 
 
+def test_split_tail_plans():
+    """Split tail: the planner's plan where 576 tiles of 64 x 64 leave a last
+    round of 64; workspace sizes for whole rounds, a partial round and fewer
+    tiles than one round; plans the library must reject."""
+    p = binding.gemm_f32_plan(1536, 1536, 1536)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3
+    assert p.split_tail == 1 and p.split_k == 4 and p.k_chunk == 384
+    assert binding.gemm_f32_workspace_bytes(1536, 1536, 1536) == 4 * 4 * 1536 * 1536
+    tail = binding.make_plan(binding.GEMM_KERNEL_DMA32_64x64_S3, 4, True)
+    # 16 x 16 = 256 tiles: one whole round, nothing split
+    assert binding.gemm_f32_plan_workspace_bytes(1024, 1024, 1024, tail) == 0
+    # 17 x 16 tiles: one tile row past a whole round
+    assert binding.gemm_f32_plan_workspace_bytes(1088, 1024, 1024, tail) == 4 * 4 * 1088 * 1024
+    # 8 x 8 tiles: fewer than a round, every tile split
+    assert binding.gemm_f32_plan_workspace_bytes(512, 512, 1024, tail) == 4 * 4 * 512 * 512
+    A, B, C = VP(0x7f0000000000), VP(0x7f1000000000), VP(0x7f2000000000)
+    bad = (binding.make_plan(binding.GEMM_KERNEL_MFMA_64x64, 2, True),
+           binding.make_plan(binding.GEMM_KERNEL_VALU_64x64, 1, True),
+           binding.gemm_plan_t(binding.GEMM_KERNEL_DMA32_64x64_S3, 2, 0, 2),
+           binding.gemm_plan_t(binding.GEMM_KERNEL_DMA32_64x64_S3, 2, 0, -1))
+    for plan in bad:
+        st = binding.raw_status("gemm_f32_with_plan", A, B, C, 1536, 1536, 1536,
+                                ctypes.byref(plan), None, 0, None)
+        assert st == binding.GEMM_ERR_INVALID_PLAN, plan
+        assert binding.gemm_f32_plan_workspace_bytes(1536, 1536, 1536, plan) == 0
+
+
 def test_explicit_split_is_clamped_to_k_steps():
     plan = binding.make_plan(binding.GEMM_KERNEL_MFMA_64x64, 1000)
     # 40 K elements = 3 K steps of 16: at most 3 ranges

@@ -263,3 +263,19 @@ def test_general_large_tile_ragged(ta, tb):
     C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=91)[0]
     got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=(2, 3, 1))
     check(got, ref, S, M, N, ldc, "256-tile ragged general")
+
+
+@pytest.mark.parametrize("ta,tb,pads", [(0, 0, (0, 0, 0)), (1, 0, (2, 3, 1)), (0, 1, (0, 0, 4)),
+                                        (1, 1, (1, 1, 2))], ids=["NN", "TN", "NT", "TT"])
+def test_general_split_tail(ta, tb, pads):
+    """1536^3, whose plan splits only the last round of tiles: the reduction
+    of the split tiles applies alpha, beta and ldc (row strides that are and
+    are not multiples of 4), the whole tiles are stored directly; every output
+    against the oracle."""
+    M = N = K = 1536
+    assert binding.gemm_f32_plan(M, N, K).split_tail == 1
+    say(f"general split tail {'TN'[ta]}{'TN'[tb]} pads {pads}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=100 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=101)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
+    check(got, ref, S, M, N, ldc, "split tail general")

@@ -115,6 +115,74 @@ def test_kernel_integers_bit_exact(kname, kid, M, K, N, split):
 
 
 # ---------------------------------------------------------------------------
+# Split tail: the tiles of whole rounds of 256 computed over all of K, only the
+# last round's tiles split into K ranges.
+
+def tile_order(tiles_m: int, tiles_n: int, group_m: int = 8):
+    """(tile row, tile column) of each tile in the kernels' tile order: groups
+    of 8 tile rows, column by column inside a group."""
+    order = []
+    for g0 in range(0, tiles_m, group_m):
+        for tn in range(tiles_n):
+            order.extend((g0 + i, tn) for i in range(min(group_m, tiles_m - g0)))
+    return order
+
+
+# (kernel, tile edge, M, K, N): 18 x 16, 17 x 18 and 17 x 17 tiles, ragged
+# edges; the last rounds hold 32, 50 and 33 tiles.
+TAIL_CASES = [("dma32_64x64_s3", 64, 1100, 777, 1000), ("dma32_128x128_w8", 128, 2100, 200, 2200),
+              ("dma32_256x256_w8_s3", 256, 4200, 60, 4300)]
+
+
+@pytest.mark.parametrize("kname,t,M,K,N", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
+@pytest.mark.parametrize("split", [2, 3, 4])
+def test_split_tail_parity_and_structure(kname, t, M, K, N, split):
+    """Every output against the oracle; tiles of the whole rounds bit-identical
+    to the unsplit plan's, tiles of the last round bit-identical to the plan
+    that splits every tile (the same K ranges, summed in the same order)."""
+    kid = binding.KERNELS[kname]
+    say(f"split tail {kname} {M}x{K}x{N} split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=M + K + N + split)
+    C_tail = run(A, B, plan=binding.make_plan(kid, split, True))
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C_tail, C_ref, S, f"{kname} tail/{split}")
+    C_one = run(A, B, plan=binding.make_plan(kid, 1))
+    C_all = run(A, B, plan=binding.make_plan(kid, split))
+    order = tile_order(-(-M // t), -(-N // t))
+    whole = len(order) // 256 * 256
+    assert 0 < whole < len(order)
+    for i, (r, c) in enumerate(order):
+        rs, cs = slice(r * t, (r + 1) * t), slice(c * t, (c + 1) * t)
+        want = C_one if i < whole else C_all
+        assert_bits_equal(C_tail[rs, cs], want[rs, cs], f"{kname} tile {i} ({r}, {c})")
+
+
+@pytest.mark.parametrize("kname,t,M,K,N", TAIL_CASES, ids=[c[0] for c in TAIL_CASES])
+def test_split_tail_integers_bit_exact(kname, t, M, K, N):
+    say(f"split tail {kname} int {M}x{K}x{N}")
+    A, B = gemm_inputs.draw(M, K, N, "int", seed=K + 5)
+    C = run(A, B, plan=binding.make_plan(binding.KERNELS[kname], 3, True))
+    C_ref = oracle.gemm_i64(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    assert_bits_equal(C, C_ref, f"{kname} tail int")
+
+
+def test_split_tail_planner_1536():
+    """1536^3: the planner splits the last round of 64 tiles of 64 x 64 four
+    ways; every output against the oracle, a rerun bit-identical, caller and
+    library workspaces bit-identical."""
+    M = N = K = 1536
+    plan = binding.gemm_f32_plan(M, N, K)
+    say(f"split tail planner 1536^3 plan {plan}")
+    assert plan.split_tail == 1 and plan.split_k > 1
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=15)
+    C1 = run(A, B)
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C1, C_ref, S, "1536^3 split tail")
+    assert_bits_equal(run(A, B), C1, "rerun")
+    assert_bits_equal(run(A, B, entry="gemm_f32_ex"), C1, "caller workspace")
+
+
+# ---------------------------------------------------------------------------
 # Memory safety, degenerate sizes, API contract.
 
 @pytest.mark.parametrize("kname,kid", KERNELS, ids=[k for k, _ in KERNELS])

@@ -3,8 +3,9 @@ replayed: every replay must equal the eager result bit for bit.
 
 The entry points with caller-owned workspaces (gemm_f32_ex,
 gemm_f32_with_plan, gemm_f32_general with a workspace) make no allocation
-and no memset, so they can be captured; the split-K case captures the
-partial-product kernel and the reduction. Between replays the test runs
+and no memset, so they can be captured; the split-K cases capture the
+partial-product kernel and the reduction (of all tiles, or of the split
+last round). Between replays the test runs
 eager work of its own and synchronises, and it changes the inputs in place
 so a replay that reused stale results would be caught.
 """
@@ -17,7 +18,9 @@ from gpu_util import say, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(1001, 513, 777, "plain"), (256, 8192, 256, "plain"), (300, 513, 260, "general")]
+# 1536^3: the plan splits only the last round of tiles (its own reduction).
+CASES = [(1001, 513, 777, "plain"), (256, 8192, 256, "plain"), (1536, 1536, 1536, "plain"),
+         (300, 513, 260, "general")]
 
 
 @pytest.mark.parametrize("M,K,N,form", CASES, ids=[f"{m}x{k}x{n}-{f}" for m, k, n, f in CASES])
