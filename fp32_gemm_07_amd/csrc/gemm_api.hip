@@ -113,7 +113,8 @@ bool resolve(int M, int N, int K, int kernel, int split_req, bool split_tail, Re
     if (dp == tiles) return resolve(M, N, K, kernel, 1, false, out);
     out->dp_tiles = dp;
   }
-  return true;
+  // Workgroup ids and tile indices are ints on the device.
+  return out->workgroups() <= INT_MAX;
 }
 
 size_t workspace_for(int M, int N, const Resolved &r) {

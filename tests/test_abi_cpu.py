@@ -96,6 +96,18 @@ def test_invalid_plans_rejected():
         binding.GEMM_ERR_INVALID_PLAN
 
 
+def test_plan_with_more_workgroups_than_an_int_rejected():
+    """16 x 16 tiles of a 2^20 x 2^20 output: 2^32 workgroups, more than the
+    device-side ids can count (rejected before any HIP call)."""
+    M = N = 1 << 20
+    plan = binding.make_plan(binding.GEMM_KERNEL_LADDER_V0, 1)
+    assert binding.gemm_f32_plan_workspace_bytes(M, N, 16, plan) == 0
+    A, B, C = VP(0x7f0000000000), VP(0x7f1000000000), VP(0x7f2000000000)
+    st = binding.raw_status("gemm_f32_with_plan", A, B, C, M, N, 16, ctypes.byref(plan), None, 0,
+                            None)
+    assert st == binding.GEMM_ERR_INVALID_PLAN
+
+
 def test_planner_choices_for_standing_workloads():
     p4 = binding.gemm_f32_plan(4096, 4096, 4096)
     assert p4.kernel == binding.GEMM_KERNEL_DMA32_256x256_W8_S3 and p4.split_k == 1
