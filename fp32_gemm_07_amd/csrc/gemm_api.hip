@@ -470,8 +470,8 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
                                                                   stream));
     case GEMM_KERNEL_DMA16_128x64:
       return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
-                                                                  stream));
+             (plain && launch_mfma<16, 128, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                   stream));
     case GEMM_KERNEL_DMA32_128x128_W8:
       return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, true>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,

@@ -323,10 +323,10 @@ def test_skinny_and_outer_products(M, K, N):
 
 def test_operand_past_2gib_offsets():
     """B of 2 GiB (32768 x 16384): an unsplit copy-fed launch would need copy
-    offsets past 2^31 bytes, so that plan runs the register-staged kernel of
-    the same tile; the planner's own plan (split K) and the general form
-    (K passes if needed) run copy-fed. All three against sampled oracle
-    entries, and the planner's and the fallback's agree within the bound."""
+    offsets past 2^31 bytes, so such a plan runs the register-staged kernel
+    of the same tile (here for the 256 x 256 and the 128 x 64 copy-fed
+    kernels); the planner's own plan (split K) and the general form (K passes
+    if needed) run copy-fed. All against sampled oracle entries."""
     t = torch()
     M, K, N = 256, 32768, 16384
     say(f"2 GiB operand {M}x{K}x{N}")
@@ -337,8 +337,10 @@ def test_operand_past_2gib_offsets():
     del B
     s = t.cuda.current_stream()
     outs = {}
-    for name, plan in (("fallback", binding.make_plan(binding.GEMM_KERNEL_DMA32_256x256_W8_S3, 1)),
-                       ("planner", binding.gemm_f32_plan(M, N, K))):
+    plans = [(f"fallback {kn}", binding.make_plan(binding.KERNELS[kn], 1))
+             for kn in ("dma32_256x256_w8_s3", "dma16_128x64")]
+    for name, plan in plans + [("planner", binding.gemm_f32_plan(M, N, K))]:
+        say(f"  {name}")
         need = binding.gemm_f32_plan_workspace_bytes(M, N, K, plan)
         ws = t.empty((max(need // 4, 1),), dtype=t.float32, device="cuda:0")
         dC = nan_buffer(M * N)
