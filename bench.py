@@ -4,9 +4,11 @@
 
 A step is one C = A x B call of the planner's plan (every kernel it launches,
 split-K reduce included) on inputs already resident in HBM. W untimed steps,
-then K timed steps between two device synchronisations; one JSON line on
-stdout. Each call is also bracketed by a HIP event pair on the stream it is
-launched on, which gives the per-launch duration used for the roofline.
+then K timed steps back to back between two device synchronisations (host
+wall clock: `value`) and between two HIP events on the stream they are
+launched on (device time / K: the mean launch duration of the roofline);
+then a short pass of up to 20 launches, each between its own event pair,
+for the spread of single launches (context only). One JSON line on stdout.
 
 The CPU baseline is the oracle (plain FP64 triple loop) run on the host's
 cores on a bounded slab of rows of the same product, scaled to TFLOP/s; the
@@ -169,21 +171,35 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: K back-to-back steps, one event pair on the launch stream
+    # around all of them (an event record between steps would add its own
+    # packet to every step), host wall clock around the same region.
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
+    region[0].record(stream)
+    for _ in range(args.steps):
         step()
-        ends[i].record(stream)
+    region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    mean_launch_ms = region[0].elapsed_time(region[1]) / args.steps
 
-    launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    # Spread of single launches (context only): a short pass with an event
+    # pair around each launch.
+    n_each = min(args.steps, 20)
+    each = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_each)]
+    for e0, e1 in each:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in each])
+
     flops = roofline.gemm_flops(M, N, K)
     value = flops * args.steps / wall / 1e12
-    achieved = flops / (launch_ms.mean() * 1e-3) / 1e12
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
     peak = roofline.PEAK_FP32_MFMA_TFLOPS
     props = torch.cuda.get_device_properties(0)
 
@@ -209,9 +225,9 @@ def main(argv=None):
             "parallelism": "1 GPU",
         },
         "pct_of_fp32_peak": round(100 * value / peak, 2),
-        "launch_ms": {"mean": round(float(launch_ms.mean()), 4),
-                      "median": round(float(np.median(launch_ms)), 4),
-                      "min": round(float(launch_ms.min()), 4)},
+        "launch_ms": {"mean": round(float(mean_launch_ms), 4),
+                      "single_launch_median": round(float(np.median(launch_ms)), 4),
+                      "single_launch_min": round(float(launch_ms.min()), 4)},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
