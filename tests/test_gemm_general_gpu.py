@@ -13,7 +13,7 @@ import pytest
 import gemm_inputs
 import oracle
 from fp32_gemm_07_amd import binding
-from gpu_util import nan_buffer, say, to_dev, torch
+from gpu_util import check, nan_buffer, run_general, say, stored, to_dev, torch
 from parity import assert_bits_equal, assert_within_bound
 
 pytestmark = pytest.mark.gpu
@@ -24,48 +24,6 @@ def _setup():
     oracle.build(force=False)
     binding.load()
     torch()
-
-
-def stored(X: np.ndarray, trans: bool, pad: int):
-    """Storage of op = X: X (trans False) or X^T, rows padded with NaN by pad
-    floats. Returns (flat storage, ld)."""
-    Y = np.ascontiguousarray(X.T if trans else X)
-    ld = Y.shape[1] + pad
-    buf = np.full((max(Y.shape[0], 1), max(ld, 1)), np.nan, np.float32)
-    buf[:Y.shape[0], :Y.shape[1]] = Y
-    return buf.ravel(), max(ld, 1)
-
-
-def run_general(ta, tb, M, N, K, alpha, X, Y, beta, C0, pads=(0, 0, 0), workspace="library"):
-    """Both sides on the same strided storage; returns (gpu flat C, oracle flat C, S)."""
-    t = torch()
-    A, lda = stored(X, ta, pads[0])
-    B, ldb = stored(Y, tb, pads[1])
-    Cst, ldc = stored(C0, False, pads[2])
-    dA, dB, dC = to_dev(A), to_dev(B), to_dev(Cst)
-    s = t.cuda.current_stream()
-    if workspace == "library":
-        binding.gemm_f32_general(ta, tb, M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc,
-                                 stream=s.cuda_stream)
-    else:
-        need = binding.gemm_f32_general_workspace_bytes(ta, tb, M, N, K, lda, ldb)
-        ws = t.empty((max(need // 4, 1),), dtype=t.float32, device="cuda:0")
-        binding.gemm_f32_general(ta, tb, M, N, K, alpha, dA, lda, dB, ldb, beta, dC, ldc, ws,
-                                 need, s.cuda_stream)
-    s.synchronize()
-    got = dC.cpu().numpy()
-    ref, S = oracle.gemm_general(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, Cst, ldc)
-    return got, ref, S, ldc
-
-
-def check(got, ref, S, M, N, ldc, what, bits=False):
-    g = got.reshape(-1, ldc)
-    r = ref.reshape(-1, ldc)
-    assert np.isnan(g[:, N:]).all(), f"{what}: padding of C written"
-    if bits:
-        assert_bits_equal(g[:M, :N], r[:M, :N], what)
-    else:
-        assert_within_bound(g[:M, :N], r[:M, :N], S, what)
 
 
 ORDERS = [(0, 0), (1, 0), (0, 1), (1, 1)]
