@@ -43,8 +43,8 @@ FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196729.5, "write_kib": 65536.0,
-        "kernel_source_sha256": "33efb740eb4f8235b03fa66d293337b55935697f4a9545f57735ce800d0ea9a9",
+        "fetch_kib": 196729.0, "write_kib": 65536.0,
+        "kernel_source_sha256": "54635350e1ac68abfd7b07dd9c8244c8d7ec387b7deb8cafb1806b8ceab3e3b5",
     },
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")

@@ -1020,6 +1020,58 @@ void valu_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
+// Sum over the `splits` slabs (`stride` floats apart) at offset `at`, in
+// ascending slab order ((w0 + w1) + w2) + ...; the loads of up to 8 slabs are
+// issued before their adds, so their latencies overlap instead of adding up.
+template <int V>
+struct SlabSum;
+
+template <>
+struct SlabSum<4> {
+  static __device__ inline floatx4 load(const float *p) {
+    return *reinterpret_cast<const floatx4 *>(p);
+  }
+  static __device__ inline floatx4 sum(const float *__restrict__ ws, long long stride,
+                                       long long at, int splits) {
+    constexpr int kBatch = 8;
+    floatx4 s = load(ws + at);
+    int p = 1;
+    for (; p + kBatch <= splits; p += kBatch) {
+      floatx4 v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) v[b] = load(ws + (long long)(p + b) * stride + at);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        s[0] = s[0] + v[b][0]; s[1] = s[1] + v[b][1]; s[2] = s[2] + v[b][2]; s[3] = s[3] + v[b][3];
+      }
+    }
+    for (; p < splits; ++p) {
+      const floatx4 v = load(ws + (long long)p * stride + at);
+      s[0] = s[0] + v[0]; s[1] = s[1] + v[1]; s[2] = s[2] + v[2]; s[3] = s[3] + v[3];
+    }
+    return s;
+  }
+};
+
+template <>
+struct SlabSum<1> {
+  static __device__ inline float sum(const float *__restrict__ ws, long long stride, long long at,
+                                     int splits) {
+    constexpr int kBatch = 8;
+    float s = ws[at];
+    int p = 1;
+    for (; p + kBatch <= splits; p += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) v[b] = ws[(long long)(p + b) * stride + at];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) s = s + v[b];
+    }
+    for (; p < splits; ++p) s = s + ws[(long long)p * stride + at];
+    return s;
+  }
+};
+
 // Split-K reduction: sum_s ws[s][e] in ascending slab order (so the result
 // does not depend on which workgroup finished first), then
 // C <- alpha * sum + beta * C (C not read when beta == 0). The slabs are
@@ -1036,11 +1088,7 @@ void splitk_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, l
     const long long first = e * V;
     float *out = dense ? C + first : C + (first / N) * ldc + first % N;
     if constexpr (V == 4) {
-      floatx4 s = *reinterpret_cast<const floatx4 *>(ws + first);
-      for (int p = 1; p < splits; ++p) {
-        const floatx4 v = *reinterpret_cast<const floatx4 *>(ws + (long long)p * count + first);
-        s[0] = s[0] + v[0]; s[1] = s[1] + v[1]; s[2] = s[2] + v[2]; s[3] = s[3] + v[3];
-      }
+      const floatx4 s = SlabSum<4>::sum(ws, count, first, splits);
       floatx4 r;
       if (beta == 0.0f) {
         r[0] = alpha * s[0]; r[1] = alpha * s[1]; r[2] = alpha * s[2]; r[3] = alpha * s[3];
@@ -1053,8 +1101,7 @@ void splitk_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, l
       }
       *reinterpret_cast<floatx4 *>(out) = r;
     } else {
-      float s = ws[first];
-      for (int p = 1; p < splits; ++p) s = s + ws[(long long)p * count + first];
+      const float s = SlabSum<1>::sum(ws, count, first, splits);
       *out = beta == 0.0f ? alpha * s : __builtin_fmaf(alpha, s, beta * *out);
     }
   }
@@ -1084,11 +1131,7 @@ void tail_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, int
     const long long w = (long long)(m0 + r) * N + n0 + c;
     float *out = C + (long long)(m0 + r) * ldc + n0 + c;
     if constexpr (V == 4) {
-      floatx4 s = *reinterpret_cast<const floatx4 *>(ws + w);
-      for (int p = 1; p < splits; ++p) {
-        const floatx4 v = *reinterpret_cast<const floatx4 *>(ws + (long long)p * slab + w);
-        s[0] = s[0] + v[0]; s[1] = s[1] + v[1]; s[2] = s[2] + v[2]; s[3] = s[3] + v[3];
-      }
+      const floatx4 s = SlabSum<4>::sum(ws, slab, w, splits);
       floatx4 o;
       if (beta == 0.0f) {
         o[0] = alpha * s[0]; o[1] = alpha * s[1]; o[2] = alpha * s[2]; o[3] = alpha * s[3];
@@ -1101,8 +1144,7 @@ void tail_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, int
       }
       *reinterpret_cast<floatx4 *>(out) = o;
     } else {
-      float s = ws[w];
-      for (int p = 1; p < splits; ++p) s = s + ws[(long long)p * slab + w];
+      const float s = SlabSum<1>::sum(ws, slab, w, splits);
       *out = beta == 0.0f ? alpha * s : __builtin_fmaf(alpha, s, beta * *out);
     }
   }
