@@ -56,6 +56,7 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_DMA16_128x64, 128, 64, 32, "dma_mfma16_f32_128x64x32_w4_s4"},
     {GEMM_KERNEL_DMA32_128x128_W8, 128, 128, 16, "dma_mfma32_f32_128x128x16_w8_s4"},
     {GEMM_KERNEL_DMA32_64x64_S3, 64, 64, 16, "dma_mfma32_f32_64x64x16_w4_s3"},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 128, 128, 16, "dma_mfma32_f32_128x128x16_w8_s3"},
     {GEMM_KERNEL_LADDER_V0, 16, 16, 16, "ladder_v0_naive_rows_along_lanes"},
     {GEMM_KERNEL_LADDER_V1, 16, 16, 16, "ladder_v1_naive_cols_along_lanes"},
     {GEMM_KERNEL_LADDER_V2, 16, 16, 16, "ladder_v2_lds_16x16x16"},
@@ -74,7 +75,7 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // split tail).
 bool is_dma_kernel(int id) {
   return (id >= GEMM_KERNEL_DMA32_256x256_W8 && id <= GEMM_KERNEL_DMA32_128x128_W8) ||
-         id == GEMM_KERNEL_DMA32_64x64_S3;
+         id == GEMM_KERNEL_DMA32_64x64_S3 || id == GEMM_KERNEL_DMA32_128x128_W8_S3;
 }
 
 struct Resolved {
@@ -179,7 +180,7 @@ struct PlanCandidate {
 };
 constexpr PlanCandidate kPlanCandidates[] = {
     {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6},
-    {GEMM_KERNEL_DMA32_128x128_W8, 0.982, 6.9, 3.9},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9},
     {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
@@ -473,7 +474,11 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
              (plain && launch_mfma<16, 128, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                    stream));
     case GEMM_KERNEL_DMA32_128x128_W8:
-      return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, true>(p, ws, r, slab, stream) ||
+      return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, false>(p, ws, r, slab, stream) ||
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+                                                                    stream));
+    case GEMM_KERNEL_DMA32_128x128_W8_S3:
+      return launch_dma<32, 128, 128, 16, 2, 4, 3, 2, true>(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_64x64_S3:

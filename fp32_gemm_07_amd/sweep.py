@@ -32,13 +32,14 @@ DEFAULT_SHAPES = [
     "8192x1024x8192", "256x8192x256", "512x131072x512", "4096x4096x4096", "6144x6144x6144",
     "8192x8192x8192",
 ]
-KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4", "dma32_128x128_w8",
+KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4", "dma32_128x128_w8_s3",
+           "dma32_128x128_w8",
            "dma16_128x128_w4",
            "dma32_64x64_s3", "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64", "mfma32_128x128",
            "mfma32_64x64", "valu_64x64"]
 SPLITS = (1, 2, 4, 8, 16, 32, 64)
 MAX_WORKSPACE = 2 << 30
-TAIL_KERNELS = {"dma32_256x256_w8_s3": 256, "dma32_128x128_w8": 128, "dma32_64x64_s3": 64}
+TAIL_KERNELS = {"dma32_256x256_w8_s3": 256, "dma32_128x128_w8_s3": 128, "dma32_64x64_s3": 64}
 
 
 def plan_label(plan) -> str:

@@ -130,7 +130,7 @@ def tile_order(tiles_m: int, tiles_n: int, group_m: int = 8):
 
 # (kernel, tile edge, M, K, N): 18 x 16, 17 x 18 and 17 x 17 tiles, ragged
 # edges; the last rounds hold 32, 50 and 33 tiles.
-TAIL_CASES = [("dma32_64x64_s3", 64, 1100, 777, 1000), ("dma32_128x128_w8", 128, 2100, 200, 2200),
+TAIL_CASES = [("dma32_64x64_s3", 64, 1100, 777, 1000), ("dma32_128x128_w8_s3", 128, 2100, 200, 2200),
               ("dma32_256x256_w8_s3", 256, 4200, 60, 4300)]
 
 
