@@ -185,7 +185,7 @@ constexpr PlanCandidate kPlanCandidates[] = {
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
-constexpr double kReduceFixedUs = 6.0;
+constexpr double kReduceFixedUs = 2.0;
 constexpr double kMaxWorkspaceBytes = 1024.0 * 1024.0 * 1024.0;
 constexpr double kHbmBytesPerUs = 5.0e6;
 

@@ -17,7 +17,9 @@
 //     loaded as 0.0f and out-of-range outputs are skipped at the store;
 //   - workgroup -> tile mapping is aware of the 8 XCDs (see map_tile);
 //   - split-K: a third index cuts K into contiguous ranges whose partial tiles
-//     go to a workspace and are summed by splitk_reduce in fixed order.
+//     go to a workspace and are summed in fixed order (splitk_reduce_kernel);
+//     the copy-fed kernel can also split only the tiles of the last, partial
+//     round of workgroups and compute the others whole (tail_reduce_kernel).
 #pragma once
 
 #include <hip/hip_runtime.h>
