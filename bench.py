@@ -43,8 +43,8 @@ FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196729.0, "write_kib": 65536.0,
-        "kernel_source_sha256": "54635350e1ac68abfd7b07dd9c8244c8d7ec387b7deb8cafb1806b8ceab3e3b5",
+        "fetch_kib": 196726.0, "write_kib": 65536.0,
+        "kernel_source_sha256": "13c6f8336a949c83cf1f0a93996071feb3ccc6f8938d9173292bfc5e89739026",
     },
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
