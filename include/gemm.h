@@ -185,7 +185,15 @@ int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, i
  * overlap A's or B's (GEMM_ERR_ALIAS). Operands whose rows are so long that
  * one 64-row tile spans 2^31 bytes are rejected (GEMM_ERR_INVALID_DIM);
  * an operand whose K range would span 2^31 bytes is processed in several
- * K passes, each after the first accumulating into C. Returns a status. */
+ * K passes, each after the first accumulating into C. Returns a status.
+ *
+ * Column-major data (the BLAS convention): a column-major r x c matrix with
+ * leading dimension ld is the row-major c x r matrix with row stride ld, its
+ * transpose, and (op(A) op(B))^T = op(B)^T op(A)^T. So the column-major
+ * product C = alpha * op(A) op(B) + beta * C (A, B, C column-major with
+ * leading dimensions lda, ldb, ldc) is
+ *   gemm_f32_general(trans_b, trans_a, N, M, K, alpha, B, ldb, A, lda, beta,
+ *                    C, ldc, ...). */
 int gemm_f32_general(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
                      int lda, const float *B, int ldb, float beta, float *C, int ldc,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);

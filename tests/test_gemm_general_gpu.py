@@ -237,3 +237,30 @@ def test_general_split_tail(ta, tb, pads):
     C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=101)[0]
     got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
     check(got, ref, S, M, N, ldc, "split tail general")
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+def test_column_major_through_swapped_operands(ta, tb):
+    """The column-major recipe of the header: A, B, C stored column-major
+    (padded leading dimensions), the call made with the operands and their
+    transpose flags swapped and M, N exchanged; the result, read back as
+    column-major, against the oracle's row-major alpha * op(A) op(B) + beta * C."""
+    t = torch()
+    M, K, N = 97, 53, 71
+    say(f"column-major {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=110 + ta + 2 * tb)   # op(A), op(B)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=111)[0]
+    # Column-major storage is row-major storage of the transpose: op(A) = A
+    # (M x K column-major) is stored as X^T row-major; op(A) = A^T means A is
+    # K x M column-major, i.e. X row-major. Likewise for B; C is X-like (M x N
+    # column-major = C^T row-major).
+    A, lda = stored(X, ta == 0, 2)
+    B, ldb = stored(Y, tb == 0, 3)
+    Cs, ldc = stored(C0.T, False, 1)
+    dA, dB, dC = to_dev(A), to_dev(B), to_dev(Cs)
+    binding.gemm_f32_general(tb, ta, N, M, K, 1.5, dB, ldb, dA, lda, -0.5, dC, ldc)
+    t.cuda.synchronize()
+    got = dC.cpu().numpy().reshape(-1, ldc)
+    assert np.isnan(got[:, M:]).all(), "padding of C written"
+    ref, S = oracle.gemm_general(0, 0, M, N, K, 1.5, X, K, Y, N, -0.5, C0, N)
+    assert_within_bound(got[:N, :M].T, ref.reshape(M, N), S.reshape(M, N), "column-major")
