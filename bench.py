@@ -137,8 +137,8 @@ def cpu_baseline(A, B, C_gpu, target_s: float):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
-              "a multi-GPU run is not part of it.", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the library "
+              "has no multi-GPU path (sharding is a design note, not code).", file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
