@@ -22,7 +22,7 @@ DMA = [k for k in binding.KERNELS if k.startswith("dma")]
 KERNEL_NAMES = list(binding.KERNELS)
 
 
-def plain_cases(n=120, seed=2024):
+def plain_cases(n=400, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -38,7 +38,7 @@ def plain_cases(n=120, seed=2024):
     return out
 
 
-def general_cases(n=60, seed=7):
+def general_cases(n=200, seed=7):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
