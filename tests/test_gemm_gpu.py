@@ -276,6 +276,57 @@ def test_non_default_stream():
     assert_within_bound(C, C_ref, S, "side stream")
 
 
+def test_calls_do_not_synchronize_the_device():
+    """Stream semantics: with a long run of work queued on one stream, calls
+    on another stream (an unsplit plan, and a split plan with a caller-owned
+    workspace) return while that work is still running, so they did not wait
+    for the device; their results are right once their own stream is done."""
+    t = torch()
+    say("no implicit device synchronisation")
+    cases = [(1001, 513, 777), (256, 8192, 256)]
+    inputs = []
+    for (M, K, N) in cases:
+        A, B = gemm_inputs.draw(M, K, N, "uniform", seed=M + N)
+        need = binding.gemm_f32_workspace_bytes(M, N, K)
+        inputs.append((M, K, N, A, B, to_dev(A), to_dev(B), nan_buffer(M * N), need,
+                       t.empty((max(need // 4, 1),), dtype=t.float32, device="cuda:0")))
+    x = t.randn(4096, 4096, device="cuda:0")
+    busy, side = t.cuda.Stream(), t.cuda.Stream()
+    t.cuda.synchronize()
+    with t.cuda.stream(busy):
+        for _ in range(60):          # tens of milliseconds of matrix products
+            y = x @ x
+    for (M, K, N, A, B, dA, dB, dC, need, ws) in inputs:
+        binding.gemm_f32_ex(dA, dB, dC, M, N, K, ws, need, side.cuda_stream)
+    still_running = not busy.query()
+    side.synchronize()
+    t.cuda.synchronize()
+    del y
+    assert still_running, "a library call waited for work on another stream"
+    for (M, K, N, A, B, dA, dB, dC, need, ws) in inputs:
+        C_ref, S = oracle.gemm(A, B)
+        assert_within_bound(dC.cpu().numpy().reshape(M, N), C_ref, S, f"{M}x{K}x{N}")
+
+
+# Sizes at tile and K-step edges (16, 32, 64, 128, 256, 512 and their
+# neighbours) and primes, crossed sparsely into (M, K, N) triples.
+EDGE_SIZES = [1, 2, 3, 7, 15, 16, 17, 31, 32, 33, 63, 64, 65, 97, 127, 128, 129, 251, 255, 256,
+              257, 509, 511, 512, 513]
+EDGE_CASES = [(EDGE_SIZES[i % 25], EDGE_SIZES[(7 * i + 3 + i // 25) % 25],
+               EDGE_SIZES[(11 * i + 5 + 3 * (i // 25)) % 25]) for i in range(50)]
+
+
+@pytest.mark.parametrize("M,K,N", EDGE_CASES, ids=[f"{m}x{k}x{n}" for m, k, n in EDGE_CASES])
+def test_edge_size_sweep_planner(M, K, N):
+    """The planner's plan (gemm_f32) on sizes at every tile and K-step edge:
+    each output against the oracle, C pre-filled with NaN."""
+    say(f"edge sweep {M}x{K}x{N} plan {binding.gemm_f32_plan(M, N, K)}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=M * 3 + K * 5 + N)
+    C = run(A, B)
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, f"{M}x{K}x{N}")
+
+
 def test_caller_workspace_matches_library_workspace():
     say("gemm_f32_ex vs gemm_f32 (split-K)")
     M, K, N = 256, 16384, 256
