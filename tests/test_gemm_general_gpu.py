@@ -264,3 +264,28 @@ def test_column_major_through_swapped_operands(ta, tb):
     assert np.isnan(got[:, M:]).all(), "padding of C written"
     ref, S = oracle.gemm_general(0, 0, M, N, K, 1.5, X, K, Y, N, -0.5, C0, N)
     assert_within_bound(got[:N, :M].T, ref.reshape(M, N), S.reshape(M, N), "column-major")
+
+
+@pytest.mark.parametrize("ta,tb", [(1, 0), (0, 1), (1, 1)], ids=["TN", "NT", "TT"])
+def test_general_long_k_full_size_sampled(ta, tb):
+    """512 x 131072 x 512 (the long-K workload, K split 16 ways) in the
+    transposed orders, alpha = 1.5, beta = -0.5: 2000 sampled outputs against
+    the oracle's entries on the explicitly transposed operands, all finite."""
+    t = torch()
+    M, K, N = 512, 131072, 512
+    say(f"general long K {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=120 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=121)[0]
+    dA = to_dev(np.ascontiguousarray(X.T) if ta else X)
+    dB = to_dev(np.ascontiguousarray(Y.T) if tb else Y)
+    dC = to_dev(C0)
+    binding.gemm_f32_general(ta, tb, M, N, K, 1.5, dA, M if ta else K, dB, K if tb else N, -0.5,
+                             dC, N)
+    t.cuda.synchronize()
+    C = dC.cpu().numpy().reshape(M, N)
+    assert np.isfinite(C).all()
+    rows, cols = gemm_inputs.sample_indices(M, N, 2000, seed=ta + 2 * tb)
+    ref, S = oracle.gemm_entries(X, Y, rows, cols)
+    want = 1.5 * ref.astype(np.float64) - 0.5 * C0[rows, cols].astype(np.float64)
+    bound_scale = 1.5 * S + 0.5 * np.abs(C0[rows, cols])
+    assert_within_bound(C[rows, cols], want, bound_scale, "general long K sampled")
