@@ -79,8 +79,9 @@ enum {
   GEMM_KERNEL_MFMA_128x128_W1 = 19,    /* mfma32, 128x128 tile, K step 16, one wave */
   GEMM_KERNEL_MFMA_64x64_W1 = 21,      /* mfma32, 64x64 tile, K step 16, one wave */
   /* Kernels fed by direct global->LDS copies through a ring of LDS stages
-   * (any K and N; shapes whose per-tile offsets would pass 2^31 bytes run the
-   * register-staged kernel of the same tile). */
+   * (any K and N). When a tile's copy offsets would pass 2^31 bytes, a plain
+   * product runs the register-staged kernel of the same tile instead, the
+   * general form runs in K passes, and a split_tail plan is rejected. */
   GEMM_KERNEL_DMA32_256x256_W8 = 30,    /* mfma32, 256x256, K step 16, 8 waves, 4 stages */
   GEMM_KERNEL_DMA32_128x128_W4 = 33,    /* mfma32, 128x128, K step 16, 4 waves, 4 stages */
   GEMM_KERNEL_DMA16_128x128_W4 = 34,    /* mfma16, 128x128, K step 16, 4 waves, 4 stages */
