@@ -504,6 +504,25 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// f(integral_constant<J>) for J = 0 .. N-1, in order.
+template <int J, int N, class F>
+__device__ inline void unroll_steps(F &&f) {
+  if constexpr (J < N) {
+    f(std::integral_constant<int, J>());
+    unroll_steps<J + 1, N>(f);
+  }
+}
+
+// f(integral_constant<R>) for the one R in [R0, RMAX] that equals r (none if
+// r is outside).
+template <int R0, int RMAX, class F>
+__device__ inline void dispatch_count(int r, F &&f) {
+  if constexpr (R0 <= RMAX) {
+    if (r == R0) f(std::integral_constant<int, R0>());
+    else dispatch_count<R0 + 1, RMAX>(r, f);
+  }
+}
+
 // Swizzle of K-contiguous rows: with 4 chunks per row (BK = 16) 16
 // consecutive rows are told apart by r % 4 (bank quarter) and (r / 4) % 4
 // (chunk); with 8 chunks per row (BK = 32) by r % 2 and (r / 2) % 8.
@@ -724,10 +743,9 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       dma_copy_soff<VEC>(rb, opb.voff[i], db, stage_byte + S::A_BYTES + opb.lds[i]);
   };
   // Copies of any step: chunks past the end of the K range read zeros.
-  auto issue_checked = [&](int step) {
+  auto issue_checked = [&](int step, unsigned stage_byte) {
     const int kr = k_end - (k_begin + step * BK);   // K elements left in this step
     const unsigned da = a_step * step, db = b_step * step;
-    const unsigned stage_byte = smem_base + static_cast<unsigned>((step % NS) * S::STAGE_BYTES);
 #pragma unroll
     for (int i = 0; i < OpA::L; ++i)
       dma_copy<VEC>(ra, opa.k_valid(i, kr) ? opa.voff[i] + da : kOutOfRange,
@@ -813,7 +831,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   barrier();  // the store into smem[0] precedes every copy
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    if (s < nk) issue_checked(s);
+    if (s < nk) issue_checked(s, smem_base + static_cast<unsigned>(s * S::STAGE_BYTES));
   wait_landed(min(NS, nk) - min(1, nk));
   zero_k_tail(0);
   barrier();
@@ -853,7 +871,52 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
     }
   };
-  // Any step, with the checks: the last steps of the K range.
+  // The last R steps of the K range, t0 .. t0+R-1 (t0 a multiple of NS, so
+  // step t0+J uses stage J % NS and, when NG is odd, fragment slots of
+  // parity J): everything the main loop knows at compile time is known here
+  // too, with the checks of the final steps (copies past the K range read
+  // zeros; no copies once the last step is issued, no wait after it).
+  auto k_step_last = [&](int t0, auto j_c, auto r_c) {
+    constexpr int J = decltype(j_c)::value, R = decltype(r_c)::value;
+    constexpr int ST = J % NS;
+    constexpr bool kMore = J + 1 < R;        // a step follows
+    constexpr bool kIssue = J + NS < R;      // step J+NS still to be copied
+    // Steps up to min(R-1, J+NS-1) have been issued; step J+1 must land.
+    constexpr int kLater = (R - 1 < J + NS - 1 ? R - 1 : J + NS - 1) - (J + 1);
+    const float *st = smem + ST * STAGE_F;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int slot = ((J & 1) * NG + g) & 1;
+      if (g < NG - 1) {
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(st, g + 1, slot ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        if constexpr (kMore) {
+          wait_vmcnt<kLater * LPW>();
+          if constexpr (J + 2 == R) zero_k_tail(t0 + J + 1);
+          barrier();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(slot, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kMore) load_frags(smem + ((ST + 1) % NS) * STAGE_F, 0, slot ^ 1);
+        if constexpr (kIssue)
+          issue_checked(t0 + J + NS, smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Any one of the last steps, with run-time stage, slot parity P, waits and
+  // checks (kernels with many accumulators: see below).
   auto k_step_tail = [&](int t, auto parity) {
     constexpr int P = decltype(parity)::value;
     const bool more = t + 1 < nk;
@@ -881,7 +944,8 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         mfma_step(slot, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (more) load_frags(smem + ((t + 1) % NS) * STAGE_F, 0, slot ^ 1);
-        if (t + NS < nk) issue_checked(t + NS);
+        if (t + NS < nk)
+          issue_checked(t + NS, smem_base + static_cast<unsigned>(((t + NS) % NS) * S::STAGE_BYTES));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 1; j < 4; ++j) mfma_step(slot, j);
@@ -900,10 +964,24 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     k_step_main(t + 2, std::integral_constant<int, 2>());
     if constexpr (NS >= 4) k_step_main(t + 3, std::integral_constant<int, 3>());
   }
-  // t is a multiple of NS here, hence even when NG is odd (NS is then even).
-  for (; t < nk; t += 2) {
-    k_step_tail(t, std::integral_constant<int, 0>());
-    if (t + 1 < nk) k_step_tail(t + 1, std::integral_constant<int, 1>());
+  // nk - t steps are left: NS+1 .. 2*NS after main-loop passes, nk (at most
+  // 2*NS) without any. t is a multiple of NS, hence even when NG is odd (NS
+  // is then even). A K step of a small register tile is short (512 clocks
+  // for one 32x32 block per wave), and the run-time stage arithmetic and
+  // branches of the looped form cost ~300 clocks of it, so such tiles get one
+  // unrolled copy of the last steps per count. With many accumulators the
+  // 2*NS copies make the register allocator spill them, and a long K step
+  // hides the looped form's cost, so those keep the loop.
+  constexpr bool kUnrolledTail = FM * FN * S::ACC + 8 * (FM + FN) <= 96;
+  if constexpr (kUnrolledTail) {
+    dispatch_count<1, 2 * NS>(nk - t, [&](auto r_c) {
+      unroll_steps<0, decltype(r_c)::value>([&](auto j_c) { k_step_last(t, j_c, r_c); });
+    });
+  } else {
+    for (; t < nk; t += 2) {
+      k_step_tail(t, std::integral_constant<int, 0>());
+      if (t + 1 < nk) k_step_tail(t + 1, std::integral_constant<int, 1>());
+    }
   }
 
   // Epilogue: accumulator v of block (fm, fn) is output row Op::row(q, v) and
