@@ -177,11 +177,12 @@ struct PlanCandidate {
   double eff;
   double per_wg_us;
   double fixed_us;
+  int slots_per_cu;   // workgroups one CU holds at once (two waves per SIMD)
 };
 constexpr PlanCandidate kPlanCandidates[] = {
-    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6},
-    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9},
-    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5},
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1},
+    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
@@ -201,7 +202,15 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   const double tile_flop = 2.0 * r.k->bm * r.k->bn;
   const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * c.eff) + c.per_wg_us;
   const double split_tiles = static_cast<double>(r.tiles_m * r.tiles_n - r.dp_tiles);
-  double us = std::ceil(split_tiles * r.splits / kNumCus) * per_wg + c.fixed_us;
+  double rounds = std::ceil(split_tiles * r.splits / kNumCus);
+  // The pieces of a split tail start as the whole tiles end, on whichever CU
+  // frees a slot first. A CU holds two workgroups of a 4-wave kernel: with
+  // more pieces than half the CUs some CU takes two of them side by side
+  // (measured at 1536^3, 256 pieces: the last ends ~6 us after the rest), so
+  // such a round is costed as two.
+  if (r.dp_tiles > 0 && c.slots_per_cu > 1 && split_tiles * r.splits > kNumCus / 2)
+    rounds = std::max(rounds, 2.0);
+  double us = rounds * per_wg + c.fixed_us;
   if (r.dp_tiles > 0)
     us += static_cast<double>(r.dp_tiles / kNumCus) *
           (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * c.eff) +

@@ -130,12 +130,14 @@ def test_planner_choices_for_standing_workloads():
 
 def test_split_tail_plans():
     """Split tail: the planner's plan where 576 tiles of 64 x 64 leave a last
-    round of 64; workspace sizes for whole rounds, a partial round and fewer
-    tiles than one round; plans the library must reject."""
+    round of 64 (split in two: 128 pieces, at most one per CU; four-way, 256
+    pieces, would put two on some CU); workspace sizes for whole rounds, a
+    partial round and fewer tiles than one round; plans the library must
+    reject."""
     p = binding.gemm_f32_plan(1536, 1536, 1536)
     assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3
-    assert p.split_tail == 1 and p.split_k == 4 and p.k_chunk == 384
-    assert binding.gemm_f32_workspace_bytes(1536, 1536, 1536) == 4 * 4 * 1536 * 1536
+    assert p.split_tail == 1 and p.split_k == 2 and p.k_chunk == 768
+    assert binding.gemm_f32_workspace_bytes(1536, 1536, 1536) == 4 * 2 * 1536 * 1536
     tail = binding.make_plan(binding.GEMM_KERNEL_DMA32_64x64_S3, 4, True)
     # 16 x 16 = 256 tiles: one whole round, nothing split
     assert binding.gemm_f32_plan_workspace_bytes(1024, 1024, 1024, tail) == 0

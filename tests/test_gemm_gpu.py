@@ -167,7 +167,7 @@ def test_split_tail_integers_bit_exact(kname, t, M, K, N):
 
 
 def test_split_tail_planner_1536():
-    """1536^3: the planner splits the last round of 64 tiles of 64 x 64 four
+    """1536^3: the planner splits the last round of 64 tiles of 64 x 64 two
     ways; every output against the oracle, a rerun bit-identical, caller and
     library workspaces bit-identical."""
     M = N = K = 1536
