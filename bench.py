@@ -8,7 +8,10 @@ then K timed steps back to back between two device synchronisations (host
 wall clock: `value`) and between two HIP events on the stream they are
 launched on (device time / K: the mean launch duration of the roofline);
 then a short pass of up to 20 launches, each between its own event pair,
-for the spread of single launches (context only). One JSON line on stdout.
+for the spread of single launches (context only), and an untimed pass of at
+least 50 ms during which a host thread samples the shader clock from the
+driver's DPM table (`device.sclk_mhz_during_steps`, with the table's top
+level as `device.max_sclk_mhz`). One JSON line on stdout.
 
 The CPU baseline is the oracle (plain FP64 triple loop) run on the host's
 cores on a bounded slab of rows of the same product, scaled to TFLOP/s; the
@@ -104,6 +107,74 @@ def copy_probe(mib: int, steps: int) -> int:
     print(json.dumps({"copy_probe_bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
                       "launches": steps, "ok": bool(torch.equal(dst, src))}), flush=True)
     return 0
+
+
+def sclk_table(props):
+    """Path of this GPU's shader-clock DPM table in sysfs (amdgpu), or None.
+    Its lines are the clock levels ("1: 2400Mhz") and, marked with '*', the
+    current clock (a level, or "S: <MHz>" between levels)."""
+    import glob
+    try:
+        dev = f"{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+        path = f"/sys/bus/pci/devices/{dev}/pp_dpm_sclk"
+        if os.path.exists(path):
+            return path
+    except AttributeError:
+        pass
+    paths = glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")
+    return paths[0] if len(paths) == 1 else None
+
+
+def read_sclk(path):
+    """(current MHz, highest level MHz) from the DPM table, None where absent."""
+    cur, top = None, None
+    try:
+        with open(path) as f:
+            for line in f:
+                head, _, rest = line.partition(":")
+                mhz = float(rest.strip().split("Mhz")[0].split("MHz")[0])
+                if "*" in rest:
+                    cur = mhz
+                if head.strip().isdigit():
+                    top = mhz if top is None else max(top, mhz)
+    except (OSError, ValueError):
+        pass
+    return cur, top
+
+
+def clock_pass(step, stream, path, min_seconds=0.05):
+    """Shader clock under the same work: steps back to back for at least
+    min_seconds (not timed) while a host thread reads the DPM table every
+    millisecond. Returns {median, min, max, samples} in MHz, or None."""
+    import threading
+    import torch
+    if path is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            cur, _ = read_sclk(path)
+            if cur is not None:
+                samples.append(cur)
+            time.sleep(0.001)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(8):
+            step()
+        stream.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"median": float(np.median(samples)), "min": min(samples), "max": max(samples),
+            "samples": len(samples)}
 
 
 def cpu_baseline(A, B, C_gpu, target_s: float):
@@ -204,11 +275,17 @@ def main(argv=None):
     torch.cuda.synchronize()
     launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in each])
 
+    # Shader clock: the table's top level, and the clock sampled during an
+    # untimed pass of the same steps (the sampling stays out of the timed one).
+    props = torch.cuda.get_device_properties(0)
+    sclk_path = sclk_table(props)
+    max_mhz = read_sclk(sclk_path)[1] if sclk_path else None
+    sustained = clock_pass(step, stream, sclk_path)
+
     flops = roofline.gemm_flops(M, N, K)
     value = flops * args.steps / wall / 1e12
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
     peak = roofline.PEAK_FP32_MFMA_TFLOPS
-    props = torch.cuda.get_device_properties(0)
 
     C = dC.cpu().numpy()
     result = {
@@ -247,7 +324,8 @@ def main(argv=None):
             "kernel": kname,
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""), "max_sclk_mhz": max_mhz,
+                   "sclk_mhz_during_steps": sustained},
         "output_finite": bool(np.isfinite(C).all()),
     }
     if not args.no_cpu_baseline:

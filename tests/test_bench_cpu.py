@@ -1,0 +1,45 @@
+"""bench.py's host-side logic (CPU only): the one-GPU guard, the HBM traffic
+table keyed by kernel source, and the shader-clock table parser."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_traffic_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
+    w, k = "square_4096", "dma_mfma32_f32_256x256x16_w8_s3"
+    m = bench.MEASURED_TRAFFIC[(w, k)]
+    want = round(bench.FETCH_FACTOR * m["fetch_kib"] * 1024 + bench.WRITE_FACTOR * m["write_kib"] * 1024)
+    # The committed table matches the committed source.
+    assert bench.measured_traffic(w, k) == want
+    # A changed source (any byte) voids it; so does an unmeasured pair.
+    other = tmp_path / "gemm_kernels.hpp"
+    other.write_bytes(open(bench.KERNEL_SOURCE, "rb").read() + b"\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(other))
+    assert bench.measured_traffic(w, k) is None
+    monkeypatch.undo()
+    assert bench.measured_traffic(w, "valu_f32_64x64x16") is None
+
+
+@pytest.mark.parametrize("text,want", [
+    ("S: 113Mhz *\n0: 500Mhz\n1: 2400Mhz\n", (113.0, 2400.0)),   # idle, between levels
+    ("0: 500Mhz\n1: 2400Mhz *\n", (2400.0, 2400.0)),             # at the top level
+    ("S: 2312Mhz *\n0: 500Mhz\n1: 2400Mhz\n", (2312.0, 2400.0)),
+    ("", (None, None)),
+])
+def test_shader_clock_table(tmp_path, text, want):
+    p = tmp_path / "pp_dpm_sclk"
+    p.write_text(text)
+    assert bench.read_sclk(str(p)) == want
+    assert bench.read_sclk(str(tmp_path / "absent")) == (None, None)
+    assert bench.clock_pass(None, None, None) is None
