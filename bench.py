@@ -8,10 +8,9 @@ then K timed steps back to back between two device synchronisations (host
 wall clock: `value`) and between two HIP events on the stream they are
 launched on (device time / K: the mean launch duration of the roofline);
 then a short pass of up to 20 launches, each between its own event pair,
-for the spread of single launches (context only), and an untimed pass of at
-least 50 ms during which a host thread samples the shader clock from the
-driver's DPM table (`device.sclk_mhz_during_steps`, with the table's top
-level as `device.max_sclk_mhz`). One JSON line on stdout.
+for the spread of single launches (context only). One JSON line on stdout,
+with the driver's top shader-clock level (`device.max_sclk_mhz`) and the
+lowest mean clock the achieved rate allows (`device.sclk_mhz_at_least`).
 
 The CPU baseline is the oracle (plain FP64 triple loop) run on the host's
 cores on a bounded slab of rows of the same product, scaled to TFLOP/s; the
@@ -142,41 +141,6 @@ def read_sclk(path):
     return cur, top
 
 
-def clock_pass(step, stream, path, min_seconds=0.05):
-    """Shader clock under the same work: steps back to back for at least
-    min_seconds (not timed) while a host thread reads the DPM table every
-    millisecond. Returns {median, min, max, samples} in MHz, or None."""
-    import threading
-    import torch
-    if path is None:
-        return None
-    samples, stop = [], threading.Event()
-
-    def sample():
-        while not stop.is_set():
-            cur, _ = read_sclk(path)
-            if cur is not None:
-                samples.append(cur)
-            time.sleep(0.001)
-
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    th = threading.Thread(target=sample, daemon=True)
-    th.start()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < min_seconds:
-        for _ in range(8):
-            step()
-        stream.synchronize()
-    stop.set()
-    th.join()
-    if not samples:
-        return None
-    return {"median": float(np.median(samples)), "min": min(samples), "max": max(samples),
-            "samples": len(samples)}
-
-
 def cpu_baseline(A, B, C_gpu, target_s: float):
     """Time the oracle on a slab of rows of the same product (bounded to about
     target_s seconds of host time); compare those rows with the GPU result."""
@@ -275,12 +239,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in each])
 
-    # Shader clock: the table's top level, and the clock sampled during an
-    # untimed pass of the same steps (the sampling stays out of the timed one).
     props = torch.cuda.get_device_properties(0)
     sclk_path = sclk_table(props)
     max_mhz = read_sclk(sclk_path)[1] if sclk_path else None
-    sustained = clock_pass(step, stream, sclk_path)
 
     flops = roofline.gemm_flops(M, N, K)
     value = flops * args.steps / wall / 1e12
@@ -325,7 +286,10 @@ def main(argv=None):
         },
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", ""), "max_sclk_mhz": max_mhz,
-                   "sclk_mhz_during_steps": sustained},
+                   # The FP32 matrix cores retire at most 256 FLOP per clock
+                   # per CU: the mean shader clock of the timed launches was at
+                   # least this.
+                   "sclk_mhz_at_least": round(achieved * 1e6 / (props.multi_processor_count * 256), 1)},
         "output_finite": bool(np.isfinite(C).all()),
     }
     if not args.no_cpu_baseline:

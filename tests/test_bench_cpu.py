@@ -42,4 +42,3 @@ def test_shader_clock_table(tmp_path, text, want):
     p.write_text(text)
     assert bench.read_sclk(str(p)) == want
     assert bench.read_sclk(str(tmp_path / "absent")) == (None, None)
-    assert bench.clock_pass(None, None, None) is None
