@@ -177,12 +177,16 @@ struct PlanCandidate {
   double eff;
   double per_wg_us;
   double fixed_us;
-  int slots_per_cu;   // workgroups one CU holds at once (two waves per SIMD)
+  int slots_per_cu;    // workgroups one CU holds at once (two waves per SIMD)
+  double eff_shared;   // eff when the launch puts more than one workgroup on a CU
 };
+// With two 64x64 workgroups on a CU each SIMD runs two waves, which hide
+// each other's waits: per-wave timestamps give 1,083 clocks per pair of K
+// steps against 1,024 of MFMA (0.945), one workgroup alone 0.91.
 constexpr PlanCandidate kPlanCandidates[] = {
-    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1},
-    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1},
-    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2},
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982},
+    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
@@ -200,8 +204,9 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   if (!resolve(M, N, K, c.kernel, split, tail, &r)) return 1e30;
   if (!dma_fits(pr, r.k->bm, r.k->bn, r.k->bk, r.k_span())) return 1e30;
   const double tile_flop = 2.0 * r.k->bm * r.k->bn;
-  const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * c.eff) + c.per_wg_us;
   const double split_tiles = static_cast<double>(r.tiles_m * r.tiles_n - r.dp_tiles);
+  const double eff = static_cast<double>(r.workgroups()) > kNumCus ? c.eff_shared : c.eff;
+  const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * eff) + c.per_wg_us;
   double rounds = std::ceil(split_tiles * r.splits / kNumCus);
   // The pieces of a split tail start as the whole tiles end, on whichever CU
   // frees a slot first. A CU holds two workgroups of a 4-wave kernel: with
@@ -213,7 +218,7 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   double us = rounds * per_wg + c.fixed_us;
   if (r.dp_tiles > 0)
     us += static_cast<double>(r.dp_tiles / kNumCus) *
-          (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * c.eff) +
+          (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * eff) +
            c.per_wg_us);
   if (r.splits > 1) {
     const double slab = 4.0 * M * static_cast<double>(N);

@@ -122,6 +122,12 @@ def test_planner_choices_for_standing_workloads():
     # 24 x 24 tiles of 256 would leave a third round 25% full: 128x128 tiles
     p = binding.gemm_f32_plan(6144, 6144, 6144)
     assert p.kernel == binding.GEMM_KERNEL_DMA32_128x128_W8_S3 and p.split_k == 1
+    # one GPU's share of a sharded 4096^3: 512 tiles of 64 x 64, two per CU at
+    # once, against 128 tiles of 128 x 128 split in two; the pairs of 64 x 64
+    # workgroups keep two waves per SIMD (measured 124.0 against 126.3 us)
+    for (M, N, K) in [(512, 4096, 4096), (1024, 2048, 4096)]:
+        p = binding.gemm_f32_plan(M, N, K)
+        assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_k == 1
     for (M, N, K) in [(128, 112, 96), (1024, 1024, 512), (1001, 777, 513), (1, 1, 1)]:
         p = binding.gemm_f32_plan(M, N, K)
         assert p.split_k >= 1 and p.k_chunk * p.split_k >= K
