@@ -166,6 +166,31 @@ def test_split_tail_integers_bit_exact(kname, t, M, K, N):
     assert_bits_equal(C, C_ref, f"{kname} tail int")
 
 
+# ---------------------------------------------------------------------------
+# The last K steps of a range run as an unrolled copy per remaining count
+# (1 .. 2 x stages) in the small-tile copy-fed kernels and as a loop in the
+# others: every count, with the last step ragged (K % 4 == 3, so the lanes
+# that copied the straddling 16-byte chunks zero its tail) and whole, for
+# every copy-fed kernel, whole K and split in two.
+
+DMA_KERNELS = [k for k in binding.KERNELS if k.startswith("dma")]
+K_STEP = {k: (32 if k in ("dma16_64x64", "dma16_128x64") else 16) for k in DMA_KERNELS}
+STEP_COUNTS = [(n, -5) for n in range(1, 17)] + [(n, 0) for n in (6, 7, 8, 10, 11, 15)]
+
+
+@pytest.mark.parametrize("kname", DMA_KERNELS)
+@pytest.mark.parametrize("steps,off", STEP_COUNTS, ids=[f"{n}{'' if o == 0 else 'r'}" for n, o in STEP_COUNTS])
+@pytest.mark.parametrize("split", [1, 2])
+def test_every_last_step_count(kname, steps, off, split):
+    K = K_STEP[kname] * steps + off
+    M, N = 70, 90
+    say(f"last steps {kname} K {K} ({steps} steps) split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=K * 3 + split)
+    C = run(A, B, plan=binding.make_plan(binding.KERNELS[kname], split))
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, f"{kname} K {K} split {split}")
+
+
 def test_split_tail_planner_1536():
     """1536^3: the planner splits the last round of 64 tiles of 64 x 64 two
     ways; every output against the oracle, a rerun bit-identical, caller and
