@@ -159,7 +159,7 @@ bool dma_tile_usable(const Problem &p, int bm, int bn, int bk) {
          (!p.tb || operand_fits(true, bn, p.ldb, 2 * bk));
 }
 
-// The planner: a cost model over three copy-fed kernels and power-of-two
+// The planner: a cost model over four copy-fed kernels and power-of-two
 // K splits, fitted to timings of those kernels over square, wide, long-K and
 // ragged shapes on one MI355X. A CU works through its share of a launch's
 // workgroups (at most n = ceil(workgroups / CUs) of them), so a launch costs
@@ -177,16 +177,24 @@ struct PlanCandidate {
   double eff;
   double per_wg_us;
   double fixed_us;
-  int slots_per_cu;    // workgroups one CU holds at once (two waves per SIMD)
-  double eff_shared;   // eff when the launch puts more than one workgroup on a CU
+  int slots_per_cu;           // workgroups one CU holds at once (two waves per SIMD)
+  double eff_shared;          // eff when the launch puts more than one workgroup on a CU
+  double per_wg_shared_us;    // per_wg then (one workgroup's store overlaps another's work)
+  bool all_orders;            // built for transposed operands too
 };
 // With two 64x64 workgroups on a CU each SIMD runs two waves, which hide
 // each other's waits: per-wave timestamps give 1,083 clocks per pair of K
-// steps against 1,024 of MFMA (0.945), one workgroup alone 0.91.
+// steps against 1,024 of MFMA (0.945), one workgroup alone 0.91. The 4-wave
+// 128x128 kernel, last, is for short K over large outputs, where the store
+// of C bounds the launch and two workgroups per CU overlap one's store with
+// the other's copies (8192 x 16 x 8192: 52.7 against 62.1 us for 256x256);
+// from K ~ 128 (4096^2) or ~ 200 (8192^2) on it loses to the others
+// (4096 x 256 x 4096: 77.2 against 73.1 us), which its eff_shared is fitted to.
 constexpr PlanCandidate kPlanCandidates[] = {
-    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966},
-    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982},
-    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935},
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966, 11.9, true},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982, 6.9, true},
+    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935, 1.2, true},
+    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, false},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
@@ -205,8 +213,10 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   if (!dma_fits(pr, r.k->bm, r.k->bn, r.k->bk, r.k_span())) return 1e30;
   const double tile_flop = 2.0 * r.k->bm * r.k->bn;
   const double split_tiles = static_cast<double>(r.tiles_m * r.tiles_n - r.dp_tiles);
-  const double eff = static_cast<double>(r.workgroups()) > kNumCus ? c.eff_shared : c.eff;
-  const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * eff) + c.per_wg_us;
+  const bool shared = static_cast<double>(r.workgroups()) > kNumCus;
+  const double eff = shared ? c.eff_shared : c.eff;
+  const double per_wg_us = shared ? c.per_wg_shared_us : c.per_wg_us;
+  const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * eff) + per_wg_us;
   double rounds = std::ceil(split_tiles * r.splits / kNumCus);
   // The pieces of a split tail start as the whole tiles end, on whichever CU
   // frees a slot first. A CU holds two workgroups of a 4-wave kernel: with
@@ -218,8 +228,7 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   double us = rounds * per_wg + c.fixed_us;
   if (r.dp_tiles > 0)
     us += static_cast<double>(r.dp_tiles / kNumCus) *
-          (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * eff) +
-           c.per_wg_us);
+          (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * eff) + per_wg_us);
   if (r.splits > 1) {
     const double slab = 4.0 * M * static_cast<double>(N);
     if (slab * r.splits > kMaxWorkspaceBytes) return 1e30;
@@ -247,6 +256,7 @@ PlanChoice plan(int M, int N, int K, const Problem *general = nullptr) {
   for (const PlanCandidate &c : kPlanCandidates) {
     if (general) {
       const KernelInfo *k = find_kernel(c.kernel);
+      if (!c.all_orders && (general->ta || general->tb)) continue;
       if (!dma_tile_usable(*general, k->bm, k->bn, k->bk)) continue;
     }
     for (int s = 1; s <= 64; s *= 2) {

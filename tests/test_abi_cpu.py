@@ -128,6 +128,13 @@ def test_planner_choices_for_standing_workloads():
     for (M, N, K) in [(512, 4096, 4096), (1024, 2048, 4096)]:
         p = binding.gemm_f32_plan(M, N, K)
         assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_k == 1
+    # short K over a large C is bound by the store of C: the 4-wave 128 x 128
+    # kernel (two workgroups per CU, one's store under the other's copies);
+    # from K ~ 128 (4096^2) on the 256 x 256 kernel again (measured both ways)
+    for (M, N, K) in [(8192, 8192, 16), (4096, 4096, 16), (16384, 4096, 16), (8192, 8192, 128)]:
+        assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_128x128_W4
+    for (M, N, K) in [(4096, 4096, 256), (8192, 8192, 256), (4001, 3999, 301)]:
+        assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_256x256_W8_S3
     for (M, N, K) in [(128, 112, 96), (1024, 1024, 512), (1001, 777, 513), (1, 1, 1)]:
         p = binding.gemm_f32_plan(M, N, K)
         assert p.split_k >= 1 and p.k_chunk * p.split_k >= K

@@ -213,7 +213,7 @@ def test_general_large_tile_ragged(ta, tb):
     """A ragged shape whose plan is the 256 x 256 kernel (its transposed-A
     form reads interleaved rows): every output against the oracle, with
     alpha, beta and padded strides."""
-    M, K, N = 4001, 77, 3999
+    M, K, N = 4001, 419, 3999
     plan = binding.gemm_f32_plan(M, N, K)
     assert binding.gemm_kernel_name(plan.kernel).startswith("dma_mfma32_f32_256x256")
     say(f"general 256-tile ragged {'TN'[ta]}{'TN'[tb]}")
@@ -237,6 +237,25 @@ def test_general_split_tail(ta, tb, pads):
     C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=101)[0]
     got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
     check(got, ref, S, M, N, ldc, "split tail general")
+
+
+@pytest.mark.parametrize("ta,tb,pads", [(0, 0, (0, 0, 0)), (0, 0, (3, 1, 2)), (1, 0, (2, 3, 1)),
+                                        (0, 1, (0, 0, 4)), (1, 1, (1, 1, 2))],
+                         ids=["NN", "NN-padded", "TN", "NT", "TT"])
+def test_general_short_k_large_output(ta, tb, pads):
+    """4096 x 16 x 4096: the plain product's plan is the 4-wave 128 x 128
+    kernel (store-bound regime), which is built for op = identity only; the
+    general form takes it for untransposed operands (with alpha, beta and row
+    strides) and another kernel for transposed ones. Every output against the
+    oracle."""
+    M = N = 4096
+    K = 16
+    assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_128x128_W4
+    say(f"general short K {'TN'[ta]}{'TN'[tb]} pads {pads}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=120 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=121)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 0.75, X, Y, 2.0, C0, pads=pads)
+    check(got, ref, S, M, N, ldc, "short K general")
 
 
 @pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
