@@ -390,7 +390,8 @@ void launch_dma_t(const Problem &p, float *ws, const Resolved &r, long long slab
 }
 
 // ALL_ORDERS: the configuration is built for transposed operands too (the
-// planner's three); the others take op(A) = A, op(B) = B only.
+// planner's 256x256, 8-wave 128x128 and 64x64 kernels); the others take
+// op(A) = A, op(B) = B only.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE,
           bool ALL_ORDERS>
 bool launch_dma(const Problem &p, float *ws, const Resolved &r, long long slab,
