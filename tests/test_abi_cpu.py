@@ -233,3 +233,19 @@ def test_general_workspace_checked():
     need_t = binding.gemm_f32_general_workspace_bytes(1, 1, M, N, K, M + 3, K + 5)
     assert need_t % (4 * M * N) == 0
     assert binding.gemm_f32_general_workspace_bytes(0, 0, M, N, K, K - 1, N) == 0   # bad lda
+
+
+def test_binding_kernel_ids_mirror_the_header():
+    """Every GEMM_KERNEL_* enumerator of include/gemm.h has the same value in
+    the binding, every one but AUTO is in the binding's kernel table, and the
+    library names each kernel distinctly."""
+    text = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    header = {m.group(1): int(m.group(2))
+              for m in re.finditer(r"\b(GEMM_KERNEL_\w+)\s*=\s*(\d+)", text)}
+    assert len(header) > 20
+    for name, value in header.items():
+        assert getattr(binding, name) == value, name
+    assert sorted(binding.KERNELS.values()) == sorted(v for n, v in header.items()
+                                                      if n != "GEMM_KERNEL_AUTO")
+    names = [binding.gemm_kernel_name(k) for k in binding.KERNELS.values()]
+    assert len(set(names)) == len(names)
