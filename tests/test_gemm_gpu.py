@@ -431,3 +431,45 @@ def test_operand_past_2gib_offsets():
     for name, C in outs.items():
         assert np.isfinite(C).all(), name
         assert_within_bound(C[rows, cols], ref, S, name)
+
+
+# ---------------------------------------------------------------------------
+# IEEE special values in the operands propagate as the definition says: each
+# output is a sum of products over all of K and nothing else, so zero-filled
+# padding, the K order inside an MFMA and split-K partial sums may neither
+# add a NaN nor hide one.
+
+SPECIAL_KERNELS = ["dma32_256x256_w8_s3", "dma32_128x128_w8_s3", "dma32_64x64_s3",
+                   "dma32_128x128_w4"]
+
+
+@pytest.mark.parametrize("kname", SPECIAL_KERNELS)
+@pytest.mark.parametrize("split", [1, 2])
+def test_special_values_propagate(kname, split):
+    """A NaN at A[i0, k0] makes all of row i0 NaN; a +Inf at B[k1, j1] makes
+    C[i, j1] = sign(A[i, k1]) * Inf, and NaN where A[i, k1] = 0 (0 * Inf);
+    every other output stays finite and within the bound of the oracle."""
+    M, K, N = 300, 700, 260
+    i0, k0, k1, j1, iz = 131, 333, 650, 97, 5
+    say(f"special values {kname} split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=77)
+    A[i0, k0] = np.nan
+    B[k1, j1] = np.inf
+    A[iz, k1] = 0.0
+    C = run(A, B, plan=binding.make_plan(binding.KERNELS[kname], split))
+    # What the definition fixes, independently of the oracle.
+    want_nan = np.zeros((M, N), dtype=bool)
+    want_nan[i0, :] = True
+    want_nan[iz, j1] = True
+    assert np.array_equal(np.isnan(C), want_nan), f"{kname}/{split}: NaN pattern"
+    col = np.delete(np.arange(M), [i0, iz])
+    assert np.array_equal(C[col, j1], np.where(A[col, k1] > 0, np.inf, -np.inf).astype(np.float32))
+    # Everything else against the oracle (which computes the same IEEE sums in FP64).
+    C_ref, S = oracle.gemm(A, B)
+    assert np.array_equal(np.isnan(C_ref), want_nan)
+    fin = np.isfinite(C_ref)
+    fin[:, j1] = False
+    assert fin.sum() == (M - 1) * (N - 1)
+    assert np.isfinite(C[fin]).all()
+    err = np.abs(C[fin].astype(np.float64) - C_ref[fin])
+    assert (err <= 1e-5 * S[fin] + 1e-6).all(), f"{kname}/{split}: worst {err.max()}"
