@@ -443,26 +443,22 @@ SPECIAL_KERNELS = ["dma32_256x256_w8_s3", "dma32_128x128_w8_s3", "dma32_64x64_s3
                    "dma32_128x128_w4"]
 
 
-@pytest.mark.parametrize("kname", SPECIAL_KERNELS)
-@pytest.mark.parametrize("split", [1, 2])
-def test_special_values_propagate(kname, split):
+def _check_special_values(kname, plan, M, K, N, i0, k0, k1, j1, zeros):
     """A NaN at A[i0, k0] makes all of row i0 NaN; a +Inf at B[k1, j1] makes
-    C[i, j1] = sign(A[i, k1]) * Inf, and NaN where A[i, k1] = 0 (0 * Inf);
-    every other output stays finite and within the bound of the oracle."""
-    M, K, N = 300, 700, 260
-    i0, k0, k1, j1, iz = 131, 333, 650, 97, 5
-    say(f"special values {kname} split {split}")
+    C[i, j1] = sign(A[i, k1]) * Inf, and NaN where A[i, k1] = 0 (0 * Inf, at
+    the rows in `zeros`); every other output stays finite and within the
+    bound of the oracle."""
     A, B = gemm_inputs.draw(M, K, N, "uniform", seed=77)
     A[i0, k0] = np.nan
     B[k1, j1] = np.inf
-    A[iz, k1] = 0.0
-    C = run(A, B, plan=binding.make_plan(binding.KERNELS[kname], split))
+    A[zeros, k1] = 0.0
+    C = run(A, B, plan=plan)
     # What the definition fixes, independently of the oracle.
     want_nan = np.zeros((M, N), dtype=bool)
     want_nan[i0, :] = True
-    want_nan[iz, j1] = True
-    assert np.array_equal(np.isnan(C), want_nan), f"{kname}/{split}: NaN pattern"
-    col = np.delete(np.arange(M), [i0, iz])
+    want_nan[zeros, j1] = True
+    assert np.array_equal(np.isnan(C), want_nan), f"{kname}: NaN pattern"
+    col = np.delete(np.arange(M), [i0, *zeros])
     assert np.array_equal(C[col, j1], np.where(A[col, k1] > 0, np.inf, -np.inf).astype(np.float32))
     # Everything else against the oracle (which computes the same IEEE sums in FP64).
     C_ref, S = oracle.gemm(A, B)
@@ -472,4 +468,23 @@ def test_special_values_propagate(kname, split):
     assert fin.sum() == (M - 1) * (N - 1)
     assert np.isfinite(C[fin]).all()
     err = np.abs(C[fin].astype(np.float64) - C_ref[fin])
-    assert (err <= 1e-5 * S[fin] + 1e-6).all(), f"{kname}/{split}: worst {err.max()}"
+    assert (err <= 1e-5 * S[fin] + 1e-6).all(), f"{kname}: worst {err.max()}"
+
+
+@pytest.mark.parametrize("kname", SPECIAL_KERNELS)
+@pytest.mark.parametrize("split", [1, 2])
+def test_special_values_propagate(kname, split):
+    say(f"special values {kname} split {split}")
+    _check_special_values(kname, binding.make_plan(binding.KERNELS[kname], split),
+                          300, 700, 260, i0=131, k0=333, k1=650, j1=97, zeros=[5])
+
+
+def test_special_values_split_tail():
+    """The split-tail plan of 1100 x 777 x 1000 on 64 x 64 tiles: tile rows
+    0-15 are whole tiles, rows 16-17 (outputs 1024-1099) are split in two
+    along K. The NaN row lies in a split tile, the Inf column crosses both
+    kinds, and the zero products sit in one of each."""
+    say("special values split tail")
+    kname = "dma32_64x64_s3"
+    _check_special_values(kname, binding.make_plan(binding.KERNELS[kname], 2, True),
+                          1100, 777, 1000, i0=1050, k0=100, k1=600, j1=517, zeros=[5, 1060])
