@@ -209,3 +209,34 @@ def test_bad_arguments_raise():
         oracle.gemm(np.zeros((2, 3), np.float32), np.zeros((4, 2), np.float32))
     with pytest.raises(RuntimeError):
         oracle.gemm_entries(np.zeros((2, 3), np.float32), np.zeros((3, 2), np.float32), [2], [0])
+
+
+def test_special_values_follow_ieee_products_and_sums():
+    """Each output is the sum over k of A[i, k] * B[k, j] and nothing else, in
+    IEEE arithmetic: a NaN in A[i0, :] makes row i0 NaN; +Inf at B[k1, j1]
+    gives sign(A[i, k1]) * Inf down column j1 and NaN where A[i, k1] = 0
+    (0 * Inf); -Inf at B[k2, j2] with a +Inf from the same row of A's k1 makes
+    NaN (Inf - Inf); every other entry is finite. Checked against Python's own
+    float arithmetic entry by entry on a tiny case."""
+    M, K, N = 6, 5, 4
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=9)
+    A = A.astype(np.float64)
+    B = B.astype(np.float64)
+    A[1, 2] = np.nan
+    B[3, 1] = np.inf
+    A[4, 3] = 0.0
+    B[0, 2] = -np.inf
+    B[3, 2] = np.inf      # column 2 gets +Inf * A[i, 3] and -Inf * A[i, 0]
+    A32, B32 = A.astype(np.float32), B.astype(np.float32)
+    C, _ = oracle.gemm(A32, B32)
+    for i in range(M):
+        for j in range(N):
+            want = 0.0
+            for k in range(K):
+                want += float(A32[i, k]) * float(B32[k, j])
+            if np.isnan(want):
+                assert np.isnan(C[i, j]), (i, j)
+            else:
+                assert C[i, j] == pytest.approx(want, rel=1e-12, abs=1e-12), (i, j)
+    assert np.isnan(C[1]).all()
+    assert np.isnan(C[4, 1]) and np.isinf(C[0, 1])
