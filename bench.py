@@ -1,20 +1,32 @@
 """Bench: FP32 GEMM throughput (2MNK/s) on one MI355X, through the C ABI.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --sweep [MxKxN ...]      plan sweep (every kernel x split)
+    python bench.py --ladder                 the walkthrough's v0..v4 rungs and the MFMA kernels
+    python bench.py --orders [MxKxN ...]     the general form in every transpose case
+    python bench.py --copy-probe-mib 256     a plain copy of known size (counter calibration)
 
 A step is one C = A x B call of the planner's plan (every kernel it launches,
-split-K reduce included) on inputs already resident in HBM. W untimed steps,
-then K timed steps back to back between two device synchronisations (host
-wall clock: `value`) and between two HIP events on the stream they are
-launched on (device time / K: the mean launch duration of the roofline);
-then a short pass of up to 20 launches, each between its own event pair,
-for the spread of single launches (context only). One JSON line on stdout,
-with the driver's top shader-clock level (`device.max_sclk_mhz`) and the
-lowest mean clock the achieved rate allows (`device.sclk_mhz_at_least`).
+split-K reduce included) on inputs already resident in HBM. First an untimed
+clock-settle pass: the same step back to back for --settle-ms of wall time
+(the chip raises its shader clock over the first ~30 ms of sustained load,
+and launches timed inside that ramp run up to 25 % slower); then W untimed
+warm-up steps; then K timed steps back to back between two device
+synchronisations (host wall clock: `value`) and between two HIP events on the
+stream they are launched on (device time / K: the mean launch duration of the
+roofline); then a short pass of up to 20 launches, each between its own event
+pair, for the spread of single launches (context only). One JSON line on
+stdout, with the driver's top shader-clock level (`device.max_sclk_mhz`) and
+the lowest mean clock the achieved rate allows (`device.sclk_mhz_at_least`).
 
 The CPU baseline is the oracle (plain FP64 triple loop) run on the host's
-cores on a bounded slab of rows of the same product, scaled to TFLOP/s; the
-same rows of the GPU result are compared with it.
+cores on a bounded slab of rows of the same product (all of C at the five
+standing workloads), scaled to TFLOP/s; the same rows of the GPU result are
+compared with it.
+
+The sweep, ladder and orders modes time many calls (median or mean of HIP
+event pairs around single launches, inputs resident, after a settle pass)
+and print one JSON line per case; they check nothing (the tests do).
 """
 from __future__ import annotations
 
@@ -77,13 +89,13 @@ def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    # The chip ramps its clock over the first ~30 ms of sustained MFMA load
-    # (per-dispatch kernel traces: 1.1-1.2 ms at first, steady after ~30
-    # dispatches at 4096^3); 50 untimed steps put the timed ones past it.
-    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle-ms", type=float, default=200.0,
+                   help="untimed back-to-back steps for at least this much wall time before the "
+                        "warm-up steps (the shader clock's ramp under sustained load)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=[w.name for w in gemm_inputs.WORKLOADS])
     p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target wall time of the oracle's CPU-baseline sample")
+                   help="bound on the wall time of the oracle's CPU-baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel", default="auto", choices=["auto", *binding.KERNELS],
                    help="time this kernel instead of the planner's choice")
@@ -91,7 +103,30 @@ def parse_args(argv=None):
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="instead of the bench, run a plain device-to-device copy of this many MiB "
                         "--steps times (calibrates the HBM byte counters against a known size)")
+    p.add_argument("--sweep", nargs="*", metavar="MxKxN",
+                   help="plan sweep over these shapes (default: a standing list)")
+    p.add_argument("--ladder", action="store_true",
+                   help="the optimisation ladder on the walkthrough's two shapes")
+    p.add_argument("--orders", nargs="*", metavar="MxKxN",
+                   help="the general form in every transpose case over these shapes")
     return p.parse_args(argv)
+
+
+def settle(step, sync, ms: float):
+    """Run step() back to back for at least `ms` milliseconds of wall time
+    (untimed), in doubling batches each ended by sync(). Returns (wall ms,
+    steps)."""
+    t0 = time.perf_counter()
+    n, batch = 0, 1
+    while True:
+        for _ in range(batch):
+            step()
+        n += batch
+        sync()
+        elapsed = (time.perf_counter() - t0) * 1e3
+        if elapsed >= ms:
+            return elapsed, n
+        batch = min(2 * batch, 4096)
 
 
 def copy_probe(mib: int, steps: int) -> int:
@@ -141,6 +176,13 @@ def read_sclk(path):
     return cur, top
 
 
+def cpu_sample_rows(M: int, rows_per_s: float, target_s: float) -> int:
+    """Rows of C the CPU baseline computes: all of them when the oracle finishes
+    C within target_s at the calibrated rate, else as many as fit (never
+    fewer than one)."""
+    return int(max(1, min(M, rows_per_s * target_s)))
+
+
 def cpu_baseline(A, B, C_gpu, target_s: float):
     """Time the oracle on a slab of rows of the same product (bounded to about
     target_s seconds of host time); compare those rows with the GPU result."""
@@ -155,9 +197,7 @@ def cpu_baseline(A, B, C_gpu, target_s: float):
     t0 = time.perf_counter()
     oracle.gemm(A[:r0], B)
     dt0 = max(time.perf_counter() - t0, 1e-6)
-    rows = int(min(M, max(r0, r0 * target_s / dt0)))
-    rows = max(threads, (rows // threads) * threads) if rows >= threads else rows
-    rows = min(rows, M)
+    rows = max(r0, cpu_sample_rows(M, r0 / dt0, target_s))
     t0 = time.perf_counter()
     C_ref, S = oracle.gemm(A[:rows], B)
     dt = time.perf_counter() - t0
@@ -169,12 +209,218 @@ def cpu_baseline(A, B, C_gpu, target_s: float):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"rows 0..{rows - 1} of C ({rows} x {N} outputs, full K = {K}), "
-                  f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, FP64 accumulation",
+        "sample": f"rows 0..{rows - 1} of C ({rows} x {N} outputs{', all of C' if rows == M else ''}, "
+                  f"full K = {K}), {flops / 1e9:.2f} GFLOP in {dt:.2f} s, FP64 accumulation",
         "seconds": dt,
         "sample_parity_worst_ratio": ratio,
     }
 
+
+# ---------------------------------------------------------------------------
+# Timing modes: sweep, ladder, orders.
+
+SWEEP_SHAPES = [
+    "128x96x112", "512x512x512", "1024x512x1024", "1001x513x777", "1024x1024x1024",
+    "2048x2048x2048", "1024x4096x1024", "2048x512x2048", "3000x3000x3000", "4096x1024x4096",
+    "8192x1024x8192", "256x8192x256", "512x131072x512", "4096x4096x4096", "6144x6144x6144",
+    "8192x8192x8192",
+]
+SWEEP_KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4",
+                 "dma32_128x128_w8_s3", "dma32_128x128_w8", "dma16_128x128_w4", "dma32_64x64_s3",
+                 "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64", "mfma32_128x128",
+                 "mfma32_64x64", "valu_64x64"]
+SWEEP_SPLITS = (1, 2, 4, 8, 16, 32, 64)
+SWEEP_MAX_WORKSPACE = 2 << 30
+# copy-fed kernels that take a split tail, by tile edge
+TAIL_KERNELS = {"dma32_256x256_w8_s3": 256, "dma32_128x128_w8_s3": 128, "dma32_64x64_s3": 64}
+
+LADDER_SHAPES = ["1024x512x1024", "1001x513x777"]
+# The walkthrough's rungs v0..v4, then the matrix-core kernels.
+LADDER = [("v0 naive, lanes along rows", "ladder_v0"), ("v1 naive, lanes along columns", "ladder_v1"),
+          ("v2 LDS tiles 16x16", "ladder_v2"), ("v3 LDS, 4 outputs per lane", "ladder_v3"),
+          ("v4 LDS, 4x4 outputs per lane", "valu_64x64"),
+          ("MFMA 32x32x2, register-staged 64x64", "mfma32_64x64"),
+          ("MFMA 32x32x2, copy-fed 64x64", "dma32_64x64_s3")]
+
+ORDER_SHAPES = ["4096x4096x4096", "1024x512x1024", "1001x513x777", "2048x1024x2048",
+                "512x131072x512"]
+
+
+def parse_shape(s: str):
+    M, K, N = (int(v) for v in s.lower().split("x"))
+    return M, K, N
+
+
+def plan_label(plan) -> str:
+    return (f"{binding.gemm_kernel_name(plan.kernel)}/S{plan.split_k}"
+            + ("t" if plan.split_tail else ""))
+
+
+class Timer:
+    """HIP event pairs around single launches on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def times_us(self, call, reps: int, warm: int = 3):
+        t = self.torch
+        for _ in range(warm):
+            call()
+        t.cuda.synchronize()
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(self.stream)
+            call()
+            e1.record(self.stream)
+        t.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+
+    def median_us(self, call, reps: int) -> float:
+        return float(np.median(self.times_us(call, reps)))
+
+
+def reps_for(flop: float) -> int:
+    """Launches to time: about 0.15 s of work, between 5 and 200."""
+    return max(5, min(200, int(0.15 / max(flop / 120e12, 1e-6))))
+
+
+def settle_gpu(torch, ms: float) -> dict:
+    """The settle pass of the timing modes: a 4096^3 product of the library,
+    back to back, for `ms` of wall time."""
+    x = torch.rand((4096, 4096), device="cuda:0")
+    y = torch.empty_like(x)
+    h = torch.cuda.current_stream().cuda_stream
+    plan = binding.gemm_f32_plan(4096, 4096, 4096)
+    el, n = settle(lambda: binding.gemm_f32_with_plan(x, x, y, 4096, 4096, 4096, plan, None, 0, h),
+                   torch.cuda.synchronize, ms)
+    return {"ms": round(el, 1), "steps": n, "product": "4096x4096x4096"}
+
+
+def vendor_matmul(torch, a, b, out):
+    torch.backends.cuda.matmul.allow_tf32 = False
+    return lambda: torch.matmul(a, b, out=out)
+
+
+def run_sweep(torch, shapes, settle_ms: float) -> int:
+    """Every kernel x split (x split tail) of each shape, the planner's plan and
+    torch.matmul in FP32 (the vendor library, context only): medians of event
+    pairs around back-to-back launches. One JSON line per shape."""
+    timer = Timer(torch)
+    h = timer.stream.cuda_stream
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    print(json.dumps({"mode": "sweep", "settle": settle_gpu(torch, settle_ms)}), flush=True)
+    for shape in shapes:
+        M, K, N = parse_shape(shape)
+        dA = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
+        dB = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+        dC = torch.empty((M, N), device="cuda")
+        flop = roofline.gemm_flops(M, N, K)
+        reps = reps_for(flop)
+
+        def plan_call(plan):
+            need = binding.gemm_f32_plan_workspace_bytes(M, N, K, plan)
+            ws = torch.empty(max(need // 4, 1), device="cuda")
+            return lambda: binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, ws, need, h)
+
+        res = []
+        for kn in SWEEP_KERNELS:
+            for sp in SWEEP_SPLITS:
+                if sp > 1 and K // sp < 256:
+                    continue
+                tails = [False]
+                if sp > 1 and kn in TAIL_KERNELS:
+                    t = TAIL_KERNELS[kn]
+                    tiles = -(-M // t) * -(-N // t)
+                    if tiles > 256 and tiles % 256:
+                        tails.append(True)
+                for tail in tails:
+                    plan = binding.make_plan(binding.KERNELS[kn], sp, tail)
+                    if binding.gemm_f32_plan_workspace_bytes(M, N, K, plan) > SWEEP_MAX_WORKSPACE:
+                        continue
+                    res.append((timer.median_us(plan_call(plan), reps),
+                                f"{kn}/S{sp}" + ("t" if tail else "")))
+        auto = binding.gemm_f32_plan(M, N, K)
+        t_auto = timer.median_us(plan_call(auto), reps)
+        t_vendor = timer.median_us(vendor_matmul(torch, dA, dB, dC), reps)
+        res.sort()
+        print(json.dumps({
+            "mode": "sweep", "shape": f"{M}x{K}x{N}", "M": M, "K": K, "N": N,
+            "planner": {"plan": plan_label(auto), "us": round(t_auto, 2),
+                        "tflops": round(flop / t_auto / 1e6, 2)},
+            "vendor_torch_matmul": {"us": round(t_vendor, 2), "tflops": round(flop / t_vendor / 1e6, 2)},
+            "fastest": [{"plan": name, "us": round(us, 2)} for us, name in res[:4]],
+            "plans_timed": len(res), "reps": reps, "timing": "median of event pairs"}), flush=True)
+    return 0
+
+
+def run_ladder(torch, settle_ms: float) -> int:
+    """Each rung of the ladder on the walkthrough's two shapes: the mean of 50
+    launches after 3 warm-ups, as in its tables. One JSON line per rung."""
+    timer = Timer(torch)
+    h = timer.stream.cuda_stream
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    print(json.dumps({"mode": "ladder", "settle": settle_gpu(torch, settle_ms)}), flush=True)
+    for shape in LADDER_SHAPES:
+        M, K, N = parse_shape(shape)
+        dA = torch.rand((M, K), device="cuda", generator=gen) * 2 - 1
+        dB = torch.rand((K, N), device="cuda", generator=gen) * 2 - 1
+        dC = torch.empty((M, N), device="cuda")
+        flop = roofline.gemm_flops(M, N, K)
+        t_vendor = float(np.mean(timer.times_us(vendor_matmul(torch, dA, dB, dC), 50)))
+        for label, kn in LADDER + [("torch.matmul FP32 (vendor library)", None)]:
+            if kn is None:
+                us, name = t_vendor, "torch.matmul"
+            else:
+                plan = binding.make_plan(binding.KERNELS[kn], 1)
+                us = float(np.mean(timer.times_us(
+                    lambda: binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, None, 0, h), 50)))
+                name = binding.gemm_kernel_name(plan.kernel)
+            print(json.dumps({"mode": "ladder", "shape": shape, "rung": label, "kernel": name,
+                              "us_mean_of_50": round(us, 2), "gflops": round(flop / us / 1e3, 1),
+                              "vendor_us_over_us": round(t_vendor / us, 4)}), flush=True)
+    return 0
+
+
+def run_orders(torch, shapes, settle_ms: float) -> int:
+    """gemm_f32_general in the four transpose cases, with alpha = 1, beta = 0
+    and alpha = 2, beta = 0.5, next to torch.matmul on the same (transposed)
+    storage: medians of event pairs. One JSON line per shape and case."""
+    timer = Timer(torch)
+    h = timer.stream.cuda_stream
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    print(json.dumps({"mode": "orders", "settle": settle_gpu(torch, settle_ms)}), flush=True)
+    for shape in shapes:
+        M, K, N = parse_shape(shape)
+        flop = roofline.gemm_flops(M, N, K)
+        reps = reps_for(flop)
+        C = torch.rand((M, N), device="cuda", generator=gen)
+        for ta, tb in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            A = torch.rand((K, M) if ta else (M, K), device="cuda", generator=gen)
+            B = torch.rand((N, K) if tb else (K, N), device="cuda", generator=gen)
+            lda, ldb = A.shape[1], B.shape[1]
+            need = binding.gemm_f32_general_workspace_bytes(ta, tb, M, N, K, lda, ldb)
+            ws = torch.empty(max(need // 4, 1), device="cuda")
+            res = {}
+            for alpha, beta in ((1.0, 0.0), (2.0, 0.5)):
+                res[(alpha, beta)] = timer.median_us(
+                    lambda: binding.gemm_f32_general(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta,
+                                                     C, N, ws, need, h), reps)
+            t_v = timer.median_us(vendor_matmul(torch, A.t() if ta else A, B.t() if tb else B, C),
+                                  reps)
+            print(json.dumps({
+                "mode": "orders", "shape": shape, "case": "NT"[ta] + "NT"[tb],
+                "alpha1_beta0": {"us": round(res[(1.0, 0.0)], 2),
+                                 "tflops": round(flop / res[(1.0, 0.0)] / 1e6, 2)},
+                "alpha2_beta0.5": {"us": round(res[(2.0, 0.5)], 2),
+                                   "tflops": round(flop / res[(2.0, 0.5)] / 1e6, 2)},
+                "vendor_torch_matmul": {"us": round(t_v, 2), "tflops": round(flop / t_v / 1e6, 2)},
+                "reps": reps, "timing": "median of event pairs"}), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------
 
 def main(argv=None):
     args = parse_args(argv)
@@ -188,6 +434,12 @@ def main(argv=None):
         return 1
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib, args.steps)
+    if args.sweep is not None:
+        return run_sweep(torch, args.sweep or SWEEP_SHAPES, args.settle_ms)
+    if args.ladder:
+        return run_ladder(torch, args.settle_ms)
+    if args.orders is not None:
+        return run_orders(torch, args.orders or ORDER_SHAPES, args.settle_ms)
     w = gemm_inputs.BY_NAME[args.workload]
     M, N, K = w.M, w.N, w.K
     if args.kernel == "auto":
@@ -209,6 +461,7 @@ def main(argv=None):
     def step():
         binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, ws, ws_bytes, h)
 
+    settle_ms, settle_steps = settle(step, torch.cuda.synchronize, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -229,15 +482,7 @@ def main(argv=None):
 
     # Spread of single launches (context only): a short pass with an event
     # pair around each launch.
-    n_each = min(args.steps, 20)
-    each = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_each)]
-    for e0, e1 in each:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    launch_ms = np.array([e0.elapsed_time(e1) for e0, e1 in each])
+    launch_ms = Timer(torch).times_us(step, min(args.steps, 20), warm=0) / 1e3
 
     props = torch.cuda.get_device_properties(0)
     sclk_path = sclk_table(props)
@@ -270,6 +515,8 @@ def main(argv=None):
             "parallelism": "1 GPU",
         },
         "pct_of_fp32_peak": round(100 * value / peak, 2),
+        # untimed, before the warm-up steps: the same step back to back
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps},
         "launch_ms": {"mean": round(float(mean_launch_ms), 4),
                       "single_launch_median": round(float(np.median(launch_ms)), 4),
                       "single_launch_min": round(float(launch_ms.min()), 4)},

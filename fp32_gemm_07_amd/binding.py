@@ -23,6 +23,7 @@ GEMM_ERR_WORKSPACE = 4
 GEMM_ERR_INVALID_PLAN = 5
 GEMM_ERR_HIP = 6
 GEMM_ERR_UNSUPPORTED_DEVICE = 7
+GEMM_ERR_CAPTURING = 8
 
 GEMM_KERNEL_AUTO = 0
 GEMM_KERNEL_MFMA_256x256 = 1
@@ -85,7 +86,7 @@ KERNELS = {
 
 # Every symbol include/gemm.h declares.
 EXPORTS = (
-    "gemm_f32", "gemm_f32_workspace_bytes", "gemm_f32_ex", "gemm_f32_plan",
+    "gemm_f32", "gemm_f32_workspace_bytes", "gemm_f32_ex", "gemm_f32_plan", "gemm_f32_plan_cus",
     "gemm_f32_plan_workspace_bytes", "gemm_f32_with_plan", "gemm_f32_general",
     "gemm_f32_general_workspace_bytes", "gemm_kernel_name", "gemm_status_string",
     "gemm_last_hip_error",
@@ -154,6 +155,8 @@ def load():
         lib.gemm_f32_ex.restype = i
         lib.gemm_f32_plan.argtypes = [i, i, i, plan_p]
         lib.gemm_f32_plan.restype = i
+        lib.gemm_f32_plan_cus.argtypes = [i, i, i, i, plan_p]
+        lib.gemm_f32_plan_cus.restype = i
         lib.gemm_f32_plan_workspace_bytes.argtypes = [i, i, i, plan_p]
         lib.gemm_f32_plan_workspace_bytes.restype = sz
         lib.gemm_f32_with_plan.argtypes = [vp, vp, vp, i, i, i, plan_p, vp, sz, vp]
@@ -207,9 +210,15 @@ def gemm_f32_plan(M: int, N: int, K: int) -> gemm_plan_t:
     return p
 
 
+def gemm_f32_plan_cus(M: int, N: int, K: int, num_cus: int) -> gemm_plan_t:
+    p = gemm_plan_t()
+    _check(load().gemm_f32_plan_cus(M, N, K, num_cus, ctypes.byref(p)), "gemm_f32_plan_cus")
+    return p
+
+
 def make_plan(kernel: int, split_k: int = 1, split_tail: bool = False) -> gemm_plan_t:
     """An explicit plan; split_tail splits only the tiles of the last, partial
-    round of 256 (copy-fed kernels only)."""
+    round of one tile per CU (copy-fed kernels only)."""
     return gemm_plan_t(kernel, split_k, 0, int(split_tail))
 
 

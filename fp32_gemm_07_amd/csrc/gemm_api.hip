@@ -23,7 +23,9 @@ int hip_fail(hipError_t e) {
   return GEMM_ERR_HIP;
 }
 
-constexpr int kNumCus = 256;
+// Compute units assumed when no device can be queried (MI355X: 256). Plans
+// for a launch use the device's own count (multiProcessorCount).
+constexpr int kDefaultCus = 256;
 
 // ---------------------------------------------------------------------------
 // Kernel configurations.
@@ -92,9 +94,10 @@ struct Resolved {
 
 // Turn (kernel, requested split, split tail) into launch geometry. The split
 // is clamped to the number of K steps; every range then holds at least one
-// element. A split tail keeps the tiles of whole rounds of kNumCus tiles
-// unsplit (with a whole number of rounds nothing is split).
-bool resolve(int M, int N, int K, int kernel, int split_req, bool split_tail, Resolved *out) {
+// element. A split tail keeps the tiles of whole rounds of `cus` tiles (one
+// per compute unit) unsplit (with a whole number of rounds nothing is split).
+bool resolve(int M, int N, int K, int kernel, int split_req, bool split_tail, int cus,
+             Resolved *out) {
   const KernelInfo *k = find_kernel(kernel);
   if (!k || split_req < 1) return false;
   if (split_tail && !is_dma_kernel(kernel)) return false;
@@ -110,8 +113,8 @@ bool resolve(int M, int N, int K, int kernel, int split_req, bool split_tail, Re
   out->splits = static_cast<int>(K > 0 ? ceil_div(K, out->k_chunk) : 1);
   if (split_tail && out->splits > 1) {
     const long long tiles = out->tiles_m * out->tiles_n;
-    const long long dp = tiles / kNumCus * kNumCus;
-    if (dp == tiles) return resolve(M, N, K, kernel, 1, false, out);
+    const long long dp = tiles / cus * cus;
+    if (dp == tiles) return resolve(M, N, K, kernel, 1, false, cus, out);
     out->dp_tiles = dp;
   }
   // Workgroup ids and tile indices are ints on the device.
@@ -205,29 +208,29 @@ constexpr double kHbmBytesPerUs = 5.0e6;
 // A (kernel, split) whose copy offsets would not fit in 32 bits is not
 // considered (the launch would fall back to a slower kernel or K passes).
 // *r_out: the geometry costed.
-double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool tail,
+double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool tail, int cus,
                     Resolved *r_out) {
   const int M = pr.M, N = pr.N, K = pr.K;
   Resolved &r = *r_out;
-  if (!resolve(M, N, K, c.kernel, split, tail, &r)) return 1e30;
+  if (!resolve(M, N, K, c.kernel, split, tail, cus, &r)) return 1e30;
   if (!dma_fits(pr, r.k->bm, r.k->bn, r.k->bk, r.k_span())) return 1e30;
   const double tile_flop = 2.0 * r.k->bm * r.k->bn;
   const double split_tiles = static_cast<double>(r.tiles_m * r.tiles_n - r.dp_tiles);
-  const bool shared = static_cast<double>(r.workgroups()) > kNumCus;
+  const bool shared = static_cast<double>(r.workgroups()) > cus;
   const double eff = shared ? c.eff_shared : c.eff;
   const double per_wg_us = shared ? c.per_wg_shared_us : c.per_wg_us;
   const double per_wg = tile_flop * r.k_chunk / (kRateCuFlopPerUs * eff) + per_wg_us;
-  double rounds = std::ceil(split_tiles * r.splits / kNumCus);
+  double rounds = std::ceil(split_tiles * r.splits / cus);
   // The pieces of a split tail start as the whole tiles end, on whichever CU
   // frees a slot first. A CU holds two workgroups of a 4-wave kernel: with
   // more pieces than half the CUs some CU takes two of them side by side
   // (measured at 1536^3, 256 pieces: the last ends ~6 us after the rest), so
   // such a round is costed as two.
-  if (r.dp_tiles > 0 && c.slots_per_cu > 1 && split_tiles * r.splits > kNumCus / 2)
+  if (r.dp_tiles > 0 && c.slots_per_cu > 1 && split_tiles * r.splits > cus / 2)
     rounds = std::max(rounds, 2.0);
   double us = rounds * per_wg + c.fixed_us;
   if (r.dp_tiles > 0)
-    us += static_cast<double>(r.dp_tiles / kNumCus) *
+    us += static_cast<double>(r.dp_tiles / cus) *
           (tile_flop * static_cast<double>(r.k_span()) / (kRateCuFlopPerUs * eff) + per_wg_us);
   if (r.splits > 1) {
     const double slab = 4.0 * M * static_cast<double>(N);
@@ -248,7 +251,7 @@ struct PlanChoice {
   bool tail;   // split only the last, partial round of tiles
 };
 
-PlanChoice plan(int M, int N, int K, const Problem *general = nullptr) {
+PlanChoice plan(int M, int N, int K, int cus, const Problem *general = nullptr) {
   PlanChoice best_plan{kPlanCandidates[0].kernel, 1, false};
   double best = 1e30;
   Problem pr = general ? *general : plain_problem(nullptr, nullptr, nullptr, M, N, K);
@@ -263,7 +266,7 @@ PlanChoice plan(int M, int N, int K, const Problem *general = nullptr) {
       if (s > 1 && K / s < 256) break;   // each K range keeps >= 256 elements
       for (int tail = 0; tail <= (s > 1 ? 1 : 0); ++tail) {
         Resolved r;
-        const double us = plan_cost_us(pr, c, s, tail != 0, &r);
+        const double us = plan_cost_us(pr, c, s, tail != 0, cus, &r);
         if (us >= 1e30) continue;
         if (r.splits < s) break;                // fewer K steps than ranges asked for
         if (tail && r.dp_tiles == 0) continue;  // the same as splitting every tile
@@ -280,27 +283,55 @@ PlanChoice plan(int M, int N, int K, const Problem *general = nullptr) {
 }
 
 // ---------------------------------------------------------------------------
-// Device check (once per device): the code objects are built for gfx950 only.
+// Per-device state, filled on first use of a device under g_mu: whether it is
+// gfx950 (the code objects are built for gfx950 only) and its compute-unit
+// count (the planner's rounds of tiles).
 std::mutex g_mu;
 constexpr int kMaxDevices = 64;
-int g_dev_ok[kMaxDevices];            // 0 unknown, 1 gfx950, -1 other
-void *g_ws[kMaxDevices];
-size_t g_ws_bytes[kMaxDevices];
+struct DeviceState {
+  int arch;          // 0 not queried yet, 1 gfx950, -1 another architecture
+  int cus;           // multiProcessorCount
+};
+DeviceState g_dev[kMaxDevices];
 
-int check_device(int *dev_out) {
+// The current device and its compute units (properties read once per device).
+hipError_t current_device(int *dev_out, int *cus_out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e);
-  if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
-  *dev_out = dev;
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_dev_ok[dev] == 0) {
+  DeviceState &d = g_dev[dev];
+  if (d.arch == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess) return hip_fail(e);
-    g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (e != hipSuccess) return e;
+    d.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kDefaultCus;
+    d.arch = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
   }
-  return g_dev_ok[dev] == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+  *dev_out = dev;
+  *cus_out = d.cus;
+  return hipSuccess;
+}
+
+// The device a launch will run on: the current one, which must be gfx950.
+int check_device(int *dev_out, int *cus_out) {
+  const hipError_t e = current_device(dev_out, cus_out);
+  if (e == hipErrorInvalidDevice) return GEMM_ERR_UNSUPPORTED_DEVICE;
+  if (e != hipSuccess) return hip_fail(e);
+  return g_dev[*dev_out].arch == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+// Compute units to plan for in a query that launches nothing: the current
+// device's, or kDefaultCus when no device can be queried (a host without a
+// GPU). Leaves the thread's last HIP error untouched.
+int planning_cus() {
+  int dev = 0, cus = kDefaultCus;
+  if (current_device(&dev, &cus) != hipSuccess) {
+    (void)hipGetLastError();
+    return kDefaultCus;
+  }
+  return cus;
 }
 
 // ---------------------------------------------------------------------------
@@ -345,26 +376,27 @@ void launch_mfma_t(const float *A, const float *B, float *out, int M, int N, int
 bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 // Picks the load width and edge-check variant of one tile configuration.
-// WPE = waves per SIMD the register allocation is sized for. Configurations
-// with SCALAR = false have no 4-byte-load variants (they would not fit their
-// register budget): they return false for shapes that need them.
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WPE, bool SCALAR>
+// WPE = waves per SIMD the register allocation of the 16-byte-load variants
+// is sized for, SWPE the same for the variants with 4-byte loads of A or B
+// (four times the staging registers); SWPE = 0: no such variants (they would
+// spill at any budget), and shapes that need them return false.
+template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int WPE, int SWPE>
 bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K,
                  const Resolved &r, long long slab, hipStream_t stream) {
   const bool va = (K % 4 == 0) && aligned16(A);
   const bool vb = (N % 4 == 0) && aligned16(B);
   const bool exact = (M % BM == 0) && (N % BN == 0) && (K % BK == 0) && (r.k_chunk % BK == 0);
-#define LGEMM_CASE(VA_, VB_, CK_)                                                             \
-  launch_mfma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, WPE, VA_, VB_, CK_>(A, B, out, M, N, K, r, \
-                                                                     slab, stream)
+#define LGEMM_CASE(W_, VA_, VB_, CK_)                                                       \
+  launch_mfma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, W_, VA_, VB_, CK_>(A, B, out, M, N, K, r, \
+                                                                    slab, stream)
   if (va && vb) {
-    if (exact) LGEMM_CASE(4, 4, false); else LGEMM_CASE(4, 4, true);
+    if (exact) LGEMM_CASE(WPE, 4, 4, false); else LGEMM_CASE(WPE, 4, 4, true);
     return true;
   }
-  if constexpr (SCALAR) {
-    if (va) LGEMM_CASE(4, 1, true);
-    else if (vb) LGEMM_CASE(1, 4, true);
-    else LGEMM_CASE(1, 1, true);
+  if constexpr (SWPE > 0) {
+    if (va) LGEMM_CASE(SWPE, 4, 1, true);
+    else if (vb) LGEMM_CASE(SWPE, 1, 4, true);
+    else LGEMM_CASE(SWPE, 1, 1, true);
     return true;
   }
 #undef LGEMM_CASE
@@ -434,81 +466,85 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
   if (!plain && !dma_kernel) return false;
   switch (r.k->id) {
     case GEMM_KERNEL_MFMA_256x256:
-      launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<32, 256, 256, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_256x256_W8:
-      if (!launch_mfma<32, 256, 256, 16, 2, 4, 2, false>(A, B, out, M, N, K, r, slab, stream))
-        launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      if (!launch_mfma<32, 256, 256, 16, 2, 4, 2, 0>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 256, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_256x128:
-      launch_mfma<32, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<32, 256, 128, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_128x128:
-      launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_64x64:
-      launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<32, 64, 64, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA16_256x128:
-      launch_mfma<16, 256, 128, 32, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<16, 256, 128, 32, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA16_128x128:
-      launch_mfma<16, 128, 128, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<16, 128, 128, 32, 2, 2, 2, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA16_64x64:
-      launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<16, 64, 64, 32, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA16_128x128_K16:
-      launch_mfma<16, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<16, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA16_256x128_K16:
-      launch_mfma<16, 256, 128, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      // Shapes that need 4-byte loads run the same 256 x 128 tile (the same
+      // geometry) with v_mfma_f32_32x32x2_f32: with them this configuration
+      // spills even at one wave per SIMD.
+      if (!launch_mfma<16, 256, 128, 16, 2, 2, 1, 0>(A, B, out, M, N, K, r, slab, stream))
+        launch_mfma<32, 256, 128, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_128x128_W1:
-      launch_mfma<32, 128, 128, 16, 1, 1, 1, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<32, 128, 128, 16, 1, 1, 1, 1>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_MFMA_64x64_W1:
-      launch_mfma<32, 64, 64, 16, 1, 1, 2, true>(A, B, out, M, N, K, r, slab, stream);
+      launch_mfma<32, 64, 64, 16, 1, 1, 2, 2>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_DMA32_256x256_W8:
       return launch_dma<32, 256, 256, 16, 2, 4, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
       return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_128x128_W4:
       return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA16_128x128_W4:
       return launch_dma<16, 128, 128, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA16_64x64:
       return launch_dma<16, 64, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA32_64x64:
       return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA16_128x64:
       return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<16, 128, 64, 32, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<16, 128, 64, 32, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                    stream));
     case GEMM_KERNEL_DMA32_128x128_W8:
       return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, false>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_128x128_W8_S3:
       return launch_dma<32, 128, 128, 16, 2, 4, 3, 2, true>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_64x64_S3:
       return launch_dma<32, 64, 64, 16, 2, 2, 3, 2, true>(p, ws, r, slab, stream) ||
-             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, true>(A, B, out, M, N, K, r, slab,
+             (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
@@ -530,8 +566,8 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));
       auto *kern = r.k->id == GEMM_KERNEL_LADDER_V0   ? gemm::ladder_naive_kernel<true>
                    : r.k->id == GEMM_KERNEL_LADDER_V1 ? gemm::ladder_naive_kernel<false>
-                   : r.k->id == GEMM_KERNEL_LADDER_V2 ? gemm::ladder_lds_kernel
-                                                      : gemm::ladder_coarse_kernel;
+                   : r.k->id == GEMM_KERNEL_LADDER_V2 ? gemm::ladder_lds_kernel<1>
+                                                      : gemm::ladder_lds_kernel<4>;
       hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, A, B, out, M, N, K, r.k_chunk,
                          (int)r.tiles_m, (int)r.tiles_n, r.splits, slab);
       return true;
@@ -543,7 +579,7 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
 // One pass of the product with a resolved plan: the kernel, then (split K)
 // the reduction of the partial slabs into C with alpha and beta, over all of
 // C or (split tail) over the split tiles only.
-int launch(const Problem &p, const Resolved &r, void *workspace, hipStream_t stream) {
+int launch(const Problem &p, const Resolved &r, void *workspace, int cus, hipStream_t stream) {
   if (!launch_gemm_kernel(p, workspace, r, stream)) return GEMM_ERR_INVALID_PLAN;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e);
@@ -571,7 +607,7 @@ int launch(const Problem &p, const Resolved &r, void *workspace, hipStream_t str
     }
     const long long items = v4 ? count / 4 : count;
     const unsigned blocks =
-        static_cast<unsigned>(std::min<long long>(ceil_div(items, gemm::kThreads), 4 * kNumCus));
+        static_cast<unsigned>(std::min<long long>(ceil_div(items, gemm::kThreads), 4LL * cus));
     if (v4)
       hipLaunchKernelGGL(gemm::splitk_reduce_kernel<4>, dim3(blocks), dim3(gemm::kThreads), 0,
                          stream, ws, p.C, count, p.N, p.ldc, r.splits, p.alpha, p.beta);
@@ -585,47 +621,169 @@ int launch(const Problem &p, const Resolved &r, void *workspace, hipStream_t str
 }
 
 // C <- beta * C (+0.0 when beta == 0): the product when K = 0 or alpha = 0.
-int launch_scale_c(const Problem &p, hipStream_t stream) {
+int launch_scale_c(const Problem &p, int cus, hipStream_t stream) {
   const long long count = (long long)p.M * p.N;
   const unsigned blocks =
-      static_cast<unsigned>(std::min<long long>(ceil_div(count, gemm::kThreads), 4 * kNumCus));
+      static_cast<unsigned>(std::min<long long>(ceil_div(count, gemm::kThreads), 4LL * cus));
   hipLaunchKernelGGL(gemm::scale_c_kernel, dim3(blocks), dim3(gemm::kThreads), 0, stream, p.C,
                      count, p.N, p.ldc, p.beta);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? GEMM_OK : hip_fail(e);
 }
 
-// The library's per-device workspace, grown to `need` bytes if possible.
-// Returns it, or null if it could not be allocated.
-void *library_workspace(int dev, size_t need, int *status) {
-  *status = GEMM_OK;
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (g_ws_bytes[dev] < need) {
-    if (g_ws[dev]) {
-      hipError_t e = hipDeviceSynchronize();
-      if (e != hipSuccess) {
-        *status = hip_fail(e);
-        return nullptr;
-      }
-      (void)hipFree(g_ws[dev]);
-      g_ws[dev] = nullptr;
-      g_ws_bytes[dev] = 0;
-    }
-    void *q = nullptr;
-    if (hipMalloc(&q, need) == hipSuccess) {
-      g_ws[dev] = q;
-      g_ws_bytes[dev] = need;
-    } else {
-      (void)hipGetLastError();
-    }
+// ---------------------------------------------------------------------------
+// The library-owned split-K workspace of gemm_f32 and gemm_f32_general (null
+// workspace argument): per device, up to kMaxWsBlocks device buffers, each
+// with an event recorded on the stream of the last work that used it. A call
+// holds g_ws_mu from choosing a buffer until its kernels and that event are
+// enqueued, so two calls never pick a buffer at the same time, and a buffer is
+// handed to new work only when nothing pending can still touch it:
+//   - its event has completed, or the last user was the same stream (stream
+//     order then puts the new work after the old), or
+//   - otherwise the new work's stream waits for the event (hipStreamWaitEvent:
+//     ordered on the device, the host does not block).
+// A buffer is freed (to make room for a larger one) only once its event has
+// completed, so no pending kernel can be reading or writing it. Nothing here
+// synchronises the device.
+std::mutex g_ws_mu;
+constexpr int kMaxWsBlocks = 8;
+struct WsBlock {
+  void *ptr;
+  size_t bytes;
+  hipEvent_t done;      // recorded after the last work that used the block
+  hipStream_t stream;   // that work's stream
+  bool recorded;        // `done` has been recorded at least once
+  bool retired;         // recording failed: never handed out again (never freed)
+};
+WsBlock g_ws[kMaxDevices][kMaxWsBlocks];
+
+// Whether nothing enqueued before can still use block b when new work is
+// enqueued on `stream`. hipStreamPerThread names a different stream on every
+// host thread, so equal handles do not imply one stream there.
+int block_free_for(const WsBlock &b, hipStream_t stream, bool *free_out) {
+  *free_out = !b.recorded || (b.stream == stream && stream != hipStreamPerThread);
+  if (*free_out) return GEMM_OK;
+  const hipError_t q = hipEventQuery(b.done);
+  if (q == hipSuccess) {
+    *free_out = true;
+    return GEMM_OK;
   }
-  return g_ws_bytes[dev] >= need ? g_ws[dev] : nullptr;
+  if (q == hipErrorNotReady) {
+    (void)hipGetLastError();
+    return GEMM_OK;
+  }
+  return hip_fail(q);
 }
 
-// Common path of the plain entry points. `plan_in` null = planner. `own_ws`:
-// use (and grow) the library's per-device workspace instead of the caller's.
+// A new block of `need` bytes in slot `b` (whose previous buffer, if any, has
+// been freed). Returns false, leaving the slot empty, if allocation fails.
+bool new_block(WsBlock &b, size_t need) {
+  void *ptr = nullptr;
+  hipEvent_t ev = nullptr;
+  if (hipMalloc(&ptr, need) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(ptr);   // never used by any kernel
+    return false;
+  }
+  b = WsBlock{ptr, need, ev, nullptr, false, false};
+  return true;
+}
+
+// Picks a block of at least `need` bytes for work about to be enqueued on
+// `stream` (g_ws_mu held), making the stream wait for the block's previous
+// user where needed. *out = null: no block could be had (the caller then runs
+// without a workspace).
+int acquire_block(int dev, size_t need, hipStream_t stream, WsBlock **out) {
+  *out = nullptr;
+  WsBlock *slots = g_ws[dev];
+  WsBlock *idle = nullptr, *busy = nullptr, *empty = nullptr, *small_idle = nullptr;
+  for (int i = 0; i < kMaxWsBlocks; ++i) {
+    WsBlock &b = slots[i];
+    if (!b.ptr) {
+      if (!empty) empty = &b;
+      continue;
+    }
+    if (b.retired) continue;
+    bool is_free = false;
+    const int st = block_free_for(b, stream, &is_free);
+    if (st != GEMM_OK) return st;
+    if (b.bytes >= need) {
+      if (is_free) {
+        if (!idle || b.bytes < idle->bytes) idle = &b;
+      } else if (!busy || b.bytes < busy->bytes) {
+        busy = &b;
+      }
+    } else if (is_free && !small_idle) {
+      small_idle = &b;
+    }
+  }
+  if (idle) {
+    *out = idle;
+    return GEMM_OK;
+  }
+  // A new buffer lets this work run alongside the busy one's.
+  if (empty && new_block(*empty, need)) {
+    *out = empty;
+    return GEMM_OK;
+  }
+  if (busy) {
+    const hipError_t e = hipStreamWaitEvent(stream, busy->done, 0);
+    if (e != hipSuccess) return hip_fail(e);
+    *out = busy;
+    return GEMM_OK;
+  }
+  // Every slot holds a smaller buffer: replace one that nothing can still use.
+  if (small_idle) {
+    const hipError_t e = hipFree(small_idle->ptr);
+    (void)hipEventDestroy(small_idle->done);
+    *small_idle = WsBlock{};
+    if (e != hipSuccess) return hip_fail(e);
+    if (new_block(*small_idle, need)) *out = small_idle;
+  }
+  return GEMM_OK;
+}
+
+// Runs body(workspace) with a library-owned workspace of at least `need` bytes
+// (body(nullptr) if none could be had), then records the block's event after
+// the enqueued work. Refuses a stream that is capturing a graph: the block
+// bookkeeping (event queries, allocation) has no meaning inside a capture.
+template <class Body>
+int with_library_workspace(int dev, size_t need, hipStream_t stream, Body &&body) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e);
+  if (cs != hipStreamCaptureStatusNone) return GEMM_ERR_CAPTURING;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  WsBlock *b = nullptr;
+  int st = acquire_block(dev, need, stream, &b);
+  if (st != GEMM_OK) return st;
+  if (!b) return body(nullptr);
+  st = body(b->ptr);
+  e = hipEventRecord(b->done, stream);
+  if (e != hipSuccess) {
+    // The block may still be in use and there is no event to tell when it
+    // is not: keep it out of the pool for good.
+    b->retired = true;
+    return st != GEMM_OK ? st : hip_fail(e);
+  }
+  b->recorded = true;
+  b->stream = stream;
+  return st;
+}
+
+// Where the split-K partial sums of a plain call go.
+enum class Ws {
+  kCaller,    // the caller's buffer (GEMM_ERR_WORKSPACE if too small)
+  kLibrary,   // the library's pool (falls back to the unsplit plan if none)
+};
+
+// Common path of the plain entry points. `plan_in` null = planner.
 int run(const float *A, const float *B, float *C, int M, int N, int K, const gemm_plan_t *plan_in,
-        void *workspace, size_t workspace_bytes, bool own_ws, hipStream_t stream) {
+        void *workspace, size_t workspace_bytes, Ws mode, hipStream_t stream) {
   int st = validate(A, B, C, M, N, K);
   if (st != GEMM_OK) return st;
   PlanChoice pc{GEMM_KERNEL_AUTO, 1, false};
@@ -636,27 +794,29 @@ int run(const float *A, const float *B, float *C, int M, int N, int K, const gem
          plan_in->split_tail > 1))
       return GEMM_ERR_INVALID_PLAN;
   }
-  if (pc.kernel == GEMM_KERNEL_AUTO) pc = plan(M, N, K);
+  const int cus = planning_cus();
+  if (pc.kernel == GEMM_KERNEL_AUTO) pc = plan(M, N, K, cus);
   Resolved r;
-  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return GEMM_ERR_INVALID_PLAN;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, cus, &r)) return GEMM_ERR_INVALID_PLAN;
   const size_t need = workspace_for(M, N, r);
-  if (!own_ws && need > 0 && (workspace == nullptr || workspace_bytes < need))
+  if (mode == Ws::kCaller && need > 0 && (workspace == nullptr || workspace_bytes < need))
     return GEMM_ERR_WORKSPACE;
   if (M == 0 || N == 0) return GEMM_OK;
 
-  int dev = 0;
-  st = check_device(&dev);
+  int dev = 0, dev_cus = 0;
+  st = check_device(&dev, &dev_cus);
   if (st != GEMM_OK) return st;
   const Problem p = plain_problem(A, B, C, M, N, K);
-  if (K == 0) return launch_scale_c(p, stream);
-
-  if (own_ws && need > 0) {
-    workspace = library_workspace(dev, need, &st);
-    if (st != GEMM_OK) return st;
-    // No workspace available: same kernel without the split.
-    if (!workspace && !resolve(M, N, K, pc.kernel, 1, false, &r)) return GEMM_ERR_INVALID_PLAN;
+  if (K == 0) return launch_scale_c(p, cus, stream);
+  if (mode == Ws::kLibrary && need > 0) {
+    return with_library_workspace(dev, need, stream, [&](void *ws) {
+      Resolved rr = r;
+      // No workspace to be had: the same kernel without the split.
+      if (!ws && !resolve(M, N, K, pc.kernel, 1, false, cus, &rr)) return (int)GEMM_ERR_INVALID_PLAN;
+      return launch(p, rr, ws, cus, stream);
+    });
   }
-  return launch(p, r, workspace, stream);
+  return launch(p, r, workspace, cus, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -687,10 +847,10 @@ int validate_general(const Problem &p) {
 // would not fit in 32 bits, K is cut into passes of *k_pass elements, run
 // one after the other (the second and later with beta = 1), and the plan is
 // made for one pass.
-bool plan_general(const Problem &p, PlanChoice *pc, int *k_pass) {
+bool plan_general(const Problem &p, int cus, PlanChoice *pc, int *k_pass) {
   long long k_eff = std::max(p.K, 1);
   for (int iter = 0; iter < 8; ++iter) {
-    *pc = plan(p.M, p.N, static_cast<int>(k_eff), &p);
+    *pc = plan(p.M, p.N, static_cast<int>(k_eff), cus, &p);
     const KernelInfo *k = find_kernel(pc->kernel);
     if (!dma_tile_usable(p, k->bm, k->bn, k->bk)) return false;
     auto fits = [&](long long kc) {
@@ -711,12 +871,12 @@ bool plan_general(const Problem &p, PlanChoice *pc, int *k_pass) {
 
 // Workspace of the general form: the largest of its passes' (the last pass
 // may be shorter and split differently).
-size_t general_workspace(const Problem &p, const PlanChoice &pc, int k_pass) {
+size_t general_workspace(const Problem &p, const PlanChoice &pc, int k_pass, int cus) {
   size_t need = 0;
   const int lens[2] = {std::min(k_pass, p.K), p.K > k_pass ? p.K % k_pass : 0};
   for (int len : lens) {
     Resolved r;
-    if (len > 0 && resolve(p.M, p.N, len, pc.kernel, pc.split, pc.tail, &r))
+    if (len > 0 && resolve(p.M, p.N, len, pc.kernel, pc.split, pc.tail, cus, &r))
       need = std::max(need, workspace_for(p.M, p.N, r));
   }
   return need;
@@ -729,34 +889,35 @@ int run_general(Problem p, void *workspace, size_t workspace_bytes, hipStream_t 
   PlanChoice pc{0, 1, false};
   int k_pass = std::max(p.K, 1);
   const bool uses_ab = p.K > 0 && p.alpha != 0.0f;
-  if (uses_ab && !plan_general(p, &pc, &k_pass)) return GEMM_ERR_INVALID_DIM;
-  const size_t need = uses_ab ? general_workspace(p, pc, k_pass) : 0;
+  const int cus = planning_cus();
+  if (uses_ab && !plan_general(p, cus, &pc, &k_pass)) return GEMM_ERR_INVALID_DIM;
+  const size_t need = uses_ab ? general_workspace(p, pc, k_pass, cus) : 0;
   const bool own_ws = workspace == nullptr;
   if (!own_ws && workspace_bytes < need) return GEMM_ERR_WORKSPACE;
 
-  int dev = 0;
-  st = check_device(&dev);
+  int dev = 0, dev_cus = 0;
+  st = check_device(&dev, &dev_cus);
   if (st != GEMM_OK) return st;
-  if (!uses_ab) return launch_scale_c(p, stream);
-  if (own_ws && need > 0) {
-    workspace = library_workspace(dev, need, &st);
-    if (st != GEMM_OK) return st;
-    if (!workspace) pc.split = 1;   // no workspace available: no split
-  }
+  if (!uses_ab) return launch_scale_c(p, cus, stream);
   // K passes: op(A)[:, k0:k0+kp] op(B)[k0:k0+kp, :], accumulated into C.
-  const float beta0 = p.beta;
-  for (int k0 = 0; k0 < p.K; k0 += k_pass) {
-    Problem q = p;
-    q.K = std::min(k_pass, p.K - k0);
-    q.A = p.A + (p.ta ? (long long)k0 * p.lda : k0);
-    q.B = p.B + (p.tb ? k0 : (long long)k0 * p.ldb);
-    q.beta = k0 == 0 ? beta0 : 1.0f;
-    Resolved r;
-    if (!resolve(q.M, q.N, q.K, pc.kernel, pc.split, pc.tail, &r)) return GEMM_ERR_INVALID_PLAN;
-    st = launch(q, r, workspace, stream);
-    if (st != GEMM_OK) return st;
-  }
-  return GEMM_OK;
+  auto passes = [&](void *ws) {
+    const int split = ws || need == 0 ? pc.split : 1;   // no workspace to be had: no split
+    const float beta0 = p.beta;
+    for (int k0 = 0; k0 < p.K; k0 += k_pass) {
+      Problem q = p;
+      q.K = std::min(k_pass, p.K - k0);
+      q.A = p.A + (p.ta ? (long long)k0 * p.lda : k0);
+      q.B = p.B + (p.tb ? k0 : (long long)k0 * p.ldb);
+      q.beta = k0 == 0 ? beta0 : 1.0f;
+      Resolved r;
+      if (!resolve(q.M, q.N, q.K, pc.kernel, split, pc.tail, cus, &r)) return (int)GEMM_ERR_INVALID_PLAN;
+      const int s2 = launch(q, r, ws, cus, stream);
+      if (s2 != GEMM_OK) return s2;
+    }
+    return (int)GEMM_OK;
+  };
+  if (own_ws && need > 0) return with_library_workspace(dev, need, stream, passes);
+  return passes(workspace);
 }
 
 }  // namespace
@@ -764,28 +925,29 @@ int run_general(Problem p, void *workspace, size_t workspace_bytes, hipStream_t 
 extern "C" {
 
 int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K, hipStream_t stream) {
-  return run(A, B, C, M, N, K, nullptr, nullptr, 0, true, stream);
+  return run(A, B, C, M, N, K, nullptr, nullptr, 0, Ws::kLibrary, stream);
 }
 
 size_t gemm_f32_workspace_bytes(int M, int N, int K) {
   if (M < 0 || N < 0 || K < 0) return 0;
-  const PlanChoice pc = plan(M, N, K);
+  const int cus = planning_cus();
+  const PlanChoice pc = plan(M, N, K, cus);
   Resolved r;
-  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return 0;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, cus, &r)) return 0;
   return workspace_for(M, N, r);
 }
 
 int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K, void *workspace,
                 size_t workspace_bytes, hipStream_t stream) {
-  return run(A, B, C, M, N, K, nullptr, workspace, workspace_bytes, false, stream);
+  return run(A, B, C, M, N, K, nullptr, workspace, workspace_bytes, Ws::kCaller, stream);
 }
 
-int gemm_f32_plan(int M, int N, int K, gemm_plan_t *out) {
+int gemm_f32_plan_cus(int M, int N, int K, int num_cus, gemm_plan_t *out) {
   if (!out) return GEMM_ERR_NULL_PTR;
-  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_DIM;
-  const PlanChoice pc = plan(M, N, K);
+  if (M < 0 || N < 0 || K < 0 || num_cus < 1) return GEMM_ERR_INVALID_DIM;
+  const PlanChoice pc = plan(M, N, K, num_cus);
   Resolved r;
-  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return GEMM_ERR_INVALID_PLAN;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, num_cus, &r)) return GEMM_ERR_INVALID_PLAN;
   out->kernel = pc.kernel;
   out->split_k = r.splits;
   out->k_chunk = r.k_chunk;
@@ -793,13 +955,20 @@ int gemm_f32_plan(int M, int N, int K, gemm_plan_t *out) {
   return GEMM_OK;
 }
 
+int gemm_f32_plan(int M, int N, int K, gemm_plan_t *out) {
+  if (!out) return GEMM_ERR_NULL_PTR;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_DIM;
+  return gemm_f32_plan_cus(M, N, K, planning_cus(), out);
+}
+
 size_t gemm_f32_plan_workspace_bytes(int M, int N, int K, const gemm_plan_t *p) {
   if (!p || M < 0 || N < 0 || K < 0) return 0;
   PlanChoice pc{p->kernel, p->split_k, p->split_tail != 0};
-  if (pc.kernel == GEMM_KERNEL_AUTO) pc = plan(M, N, K);
+  const int cus = planning_cus();
+  if (pc.kernel == GEMM_KERNEL_AUTO) pc = plan(M, N, K, cus);
   else if (p->split_tail < 0 || p->split_tail > 1) return 0;
   Resolved r;
-  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, &r)) return 0;
+  if (!resolve(M, N, K, pc.kernel, pc.split, pc.tail, cus, &r)) return 0;
   return workspace_for(M, N, r);
 }
 
@@ -807,7 +976,7 @@ int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, i
                        const gemm_plan_t *p, void *workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   if (!p) return GEMM_ERR_INVALID_PLAN;
-  return run(A, B, C, M, N, K, p, workspace, workspace_bytes, false, stream);
+  return run(A, B, C, M, N, K, p, workspace, workspace_bytes, Ws::kCaller, stream);
 }
 
 int gemm_f32_general(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A,
@@ -828,8 +997,9 @@ size_t gemm_f32_general_workspace_bytes(int trans_a, int trans_b, int M, int N, 
   if (M == 0 || N == 0 || K == 0) return 0;
   PlanChoice pc{0, 1, false};
   int k_pass = K;
-  if (!plan_general(p, &pc, &k_pass)) return 0;
-  return general_workspace(p, pc, k_pass);
+  const int cus = planning_cus();
+  if (!plan_general(p, cus, &pc, &k_pass)) return 0;
+  return general_workspace(p, pc, k_pass, cus);
 }
 
 const char *gemm_kernel_name(int kernel) {
@@ -848,6 +1018,9 @@ const char *gemm_status_string(int status) {
     case GEMM_ERR_INVALID_PLAN: return "invalid plan (unknown kernel or split < 1)";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
+    case GEMM_ERR_CAPTURING:
+      return "stream is capturing a graph and the plan needs the library's workspace "
+             "(pass a workspace instead)";
     default: return "unknown status";
   }
 }

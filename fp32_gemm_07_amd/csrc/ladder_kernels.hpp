@@ -13,10 +13,11 @@
 //   v1: one output per lane, tx along the columns: 16 consecutive floats of
 //       a B row per k, A values shared by 16 lanes;
 //   v2: 16 x 16 tiles of A and B staged in LDS per 16-wide K phase, zero
-//       filled past the edges, two barriers per phase (also the tiling
-//       section of the euler0525 post and hpc.payai.win lesson 10);
+//       filled past the edges, two barriers per phase (the tiling the
+//       euler0525 post and hpc.payai.win lesson 10 also teach);
 //   v3: each lane computes 4 consecutive outputs of one row (register
-//       coarsening along N), 16 x 64 output tile, 16-wide K phases in LDS.
+//       coarsening along N), 16 x 64 output tile, 16-wide K phases in LDS;
+//       v2 is the same kernel with one output per lane.
 // The walkthrough's v4 (a 2-D register tile per lane) is valu_gemm_kernel in
 // gemm_kernels.hpp.
 #pragma once
@@ -68,43 +69,22 @@ void ladder_naive_kernel(const float *__restrict__ A, const float *__restrict__ 
   C[(long long)tc.split * slab + (long long)row * N + col] = sum;
 }
 
-// v2: 16 x 16 outputs per workgroup, one per lane; A and B tiles of 16 x 16
-// in LDS per K phase.
+// v2 (TN = 1) and v3 (TN = 4): 16 x (16 * TN) outputs per workgroup; lane
+// (tx, ty) computes row ty, columns TN*tx .. TN*tx+TN-1 (v2: one output per
+// lane, v3: register coarsening along N). Per K phase of 16 the A tile
+// (16 x 16) takes one load per lane and the B tile (16 x 16*TN) TN loads,
+// lanes along its rows (coalesced); both are zero filled past the edges of
+// the K range and of A and B, and every lane reaches both barriers of the
+// phase (hpc.payai.win lesson 10, sections 2 and 3: the write of the tiles is
+// published by the first, their reuse is held off by the second).
+template <int TN>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void ladder_lds_kernel(const float *__restrict__ A, const float *__restrict__ B,
                        float *__restrict__ C, int M, int N, int K, int k_chunk, int tiles_m,
                        int tiles_n, int splits, long long slab) {
   (void)splits;
-  __shared__ float As[16][16];
-  __shared__ float Bs[16][16];
-  const LadderTile tc = ladder_tile<false>(blockIdx.x, tiles_m, tiles_n);
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  const int row = tc.tm * 16 + ty, col = tc.tn * 16 + tx;
-  const int k_begin = tc.split * k_chunk;
-  const int k_end = min(K, k_begin + k_chunk);
-  float sum = 0.0f;
-  // Every lane stays to every barrier; lanes outside C load zeros.
-  for (int k0 = k_begin; k0 < k_end; k0 += 16) {
-    const int ka = k0 + tx, kb = k0 + ty;
-    As[ty][tx] = (row < M && ka < k_end) ? A[(long long)row * K + ka] : 0.0f;
-    Bs[ty][tx] = (kb < k_end && col < N) ? B[(long long)kb * N + col] : 0.0f;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) sum += As[ty][k] * Bs[k][tx];
-    __syncthreads();
-  }
-  if (row < M && col < N) C[(long long)tc.split * slab + (long long)row * N + col] = sum;
-}
-
-// v3: 16 x 64 outputs per workgroup; lane (tx, ty) computes row ty, columns
-// 4*tx .. 4*tx+3. Per K phase the A tile (16 x 16) takes one load per lane
-// and the B tile (16 x 64) four.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void ladder_coarse_kernel(const float *__restrict__ A, const float *__restrict__ B,
-                          float *__restrict__ C, int M, int N, int K, int k_chunk, int tiles_m,
-                          int tiles_n, int splits, long long slab) {
-  (void)splits;
-  constexpr int BN = 64, TN = 4;
+  static_assert(TN == 1 || TN == 4, "v2 or v3");
+  constexpr int BN = 16 * TN;
   __shared__ float As[16][16];
   __shared__ __attribute__((aligned(16))) float Bs[16][BN];
   const LadderTile tc = ladder_tile<false>(blockIdx.x, tiles_m, tiles_n);
@@ -113,11 +93,13 @@ void ladder_coarse_kernel(const float *__restrict__ A, const float *__restrict__
   const int col0 = tc.tn * BN + TN * tx;
   const int k_begin = tc.split * k_chunk;
   const int k_end = min(K, k_begin + k_chunk);
-  float acc[TN] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) acc[j] = 0.0f;
   for (int k0 = k_begin; k0 < k_end; k0 += 16) {
     const int ka = k0 + tx;
     As[ty][tx] = (row < M && ka < k_end) ? A[(long long)row * K + ka] : 0.0f;
-    // B tile: element e = j*256 + lane, row e / 64, column e % 64 (coalesced).
+    // B tile: element e = j*256 + lane, row e / BN, column e % BN.
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int e = j * 256 + threadIdx.x;

@@ -29,12 +29,19 @@
  *     (A and B may overlap each other). Pointers the call does not access
  *     (all three when M or N is 0, A and B when K is 0) may be null.
  *   - Errors are reported only through the returned status; nothing is
- *     printed and nothing is thrown. Argument checks run before any HIP call,
- *     so a rejected call has enqueued nothing.
- *   - Thread-safe. The library-owned split-K workspace of gemm_f32 is one
- *     buffer per device: gemm_f32 calls on one device that overlap in time on
- *     different streams and both use split-K must be ordered by the caller
- *     (or use gemm_f32_ex with their own workspaces).
+ *     printed and nothing is thrown. Argument checks run before anything is
+ *     enqueued (the only HIP calls before them query the current device and
+ *     its properties), so a rejected call has enqueued nothing.
+ *   - Thread-safe and reentrant: calls may be made from several host threads
+ *     and on several streams at once. The library-owned split-K workspace
+ *     (gemm_f32, gemm_f32_general with a null workspace) is a small pool of
+ *     device buffers per device; a call takes a buffer that no pending work
+ *     can still use, or makes its stream wait (on the device, through an
+ *     event) for the buffer's previous user. No entry point synchronises the
+ *     device or blocks the host on GPU work.
+ *   - Plans depend on the current device's compute-unit count (its
+ *     multiProcessorCount; 256 on MI355X); query functions that launch
+ *     nothing plan for 256 when no device can be queried.
  */
 #ifndef LIBGEMM_GEMM_H
 #define LIBGEMM_GEMM_H
@@ -56,7 +63,11 @@ enum {
   GEMM_ERR_WORKSPACE = 4,        /* workspace missing or smaller than required */
   GEMM_ERR_INVALID_PLAN = 5,     /* unknown kernel id, split count < 1 or unusable split_tail */
   GEMM_ERR_HIP = 6,              /* a HIP call failed; see gemm_last_hip_error() */
-  GEMM_ERR_UNSUPPORTED_DEVICE = 7 /* the current device is not gfx950 */
+  GEMM_ERR_UNSUPPORTED_DEVICE = 7, /* the current device is not gfx950 */
+  GEMM_ERR_CAPTURING = 8          /* the stream is capturing a graph and the plan
+                                     needs the library-owned workspace (pass a
+                                     workspace: gemm_f32_ex, gemm_f32_with_plan,
+                                     gemm_f32_general) */
 };
 
 /* Kernel identifiers for explicit plans. Tile = the BM x BN output block one
@@ -69,13 +80,16 @@ enum {
   GEMM_KERNEL_MFMA_256x128 = 2,    /* mfma32, 256x128 tile, K step 16, 4 waves of 128x64 */
   GEMM_KERNEL_MFMA_128x128 = 3,    /* mfma32, 128x128 tile, K step 16, 4 waves of 64x64 */
   GEMM_KERNEL_MFMA_64x64 = 4,      /* mfma32, 64x64 tile, K step 16, 4 waves of 32x32 */
-  GEMM_KERNEL_MFMA_256x256_W8 = 5, /* mfma32, 256x256 tile, K step 16, 8 waves of 128x64 */
+  GEMM_KERNEL_MFMA_256x256_W8 = 5, /* mfma32, 256x256 tile, K step 16, 8 waves of 128x64
+                                      (shapes needing 4-byte loads: the 4-wave kernel) */
   GEMM_KERNEL_VALU_64x64 = 10,     /* vector FMA, 64x64 tile, K step 16, 4x4 outputs per lane */
   GEMM_KERNEL_MFMA16_256x128 = 13,    /* mfma16, 256x128 tile, K step 32, 4 waves of 128x64 */
   GEMM_KERNEL_MFMA16_128x128 = 14,    /* mfma16, 128x128 tile, K step 32, 4 waves of 64x64 */
   GEMM_KERNEL_MFMA16_64x64 = 15,      /* mfma16, 64x64 tile, K step 32, 4 waves of 32x32 */
   GEMM_KERNEL_MFMA16_128x128_K16 = 17, /* mfma16, 128x128 tile, K step 16, 4 waves of 64x64 */
-  GEMM_KERNEL_MFMA16_256x128_K16 = 18, /* mfma16, 256x128 tile, K step 16, 4 waves of 128x64 */
+  GEMM_KERNEL_MFMA16_256x128_K16 = 18, /* mfma16, 256x128 tile, K step 16, 4 waves of 128x64
+                                          (K or N not a multiple of 4, or A or B not
+                                          16-byte aligned: the mfma32 kernel of this tile) */
   GEMM_KERNEL_MFMA_128x128_W1 = 19,    /* mfma32, 128x128 tile, K step 16, one wave */
   GEMM_KERNEL_MFMA_64x64_W1 = 21,      /* mfma32, 64x64 tile, K step 16, one wave */
   /* Kernels fed by direct global->LDS copies through a ring of LDS stages
@@ -106,11 +120,11 @@ enum {
  *
  * split_tail = 0: every output tile is split into split_k K ranges.
  * split_tail = 1 (copy-fed kernels, ids 30-39, 45 and 46, only): the output tiles
- * are taken in rounds of 256 (one per CU); the tiles of the whole rounds are
+ * are taken in rounds of one per CU (256 on MI355X); the tiles of the whole rounds are
  * computed over all of K and stored straight into C, and only the tiles of
  * the last, partial round are split into split_k K ranges, so that the last
- * round's work is spread over all CUs. With fewer than 256 tiles this is the
- * same as split_tail = 0; with a multiple of 256 tiles nothing is split. */
+ * round's work is spread over all CUs. With fewer tiles than CUs this is the
+ * same as split_tail = 0; with a whole number of rounds nothing is split. */
 typedef struct gemm_plan {
   int kernel;
   int split_k;
@@ -119,10 +133,15 @@ typedef struct gemm_plan {
 } gemm_plan_t;
 
 /* C = A x B with the planner's choice of kernel and split. When that plan
- * splits K, the partial sums go to a library-owned per-device workspace that
- * is allocated (hipMalloc) on first need and grown when a larger one is
- * needed; if that allocation fails the call falls back to an unsplit plan.
- * Returns a status code. */
+ * splits K, the partial sums go to a library-owned workspace: per device, up
+ * to 8 buffers allocated (hipMalloc) on first need, each reused once the
+ * work that last used it has completed or is ordered before this call's on
+ * the same stream; calls that overlap on other streams get a buffer of their
+ * own or wait for one on the device. A buffer is freed only to make room for
+ * a larger one, and only once no pending work can use it. If no buffer can
+ * be had the call runs the plan's kernel unsplit. Not for graph capture when
+ * the plan splits K (GEMM_ERR_CAPTURING): pass a workspace (gemm_f32_ex)
+ * there. Returns a status code. */
 int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K,
              hipStream_t stream);
 
@@ -139,8 +158,15 @@ size_t gemm_f32_workspace_bytes(int M, int N, int K);
 int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K,
                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The planner's plan for (M, N, K), written to *plan. Returns a status code. */
+/* The planner's plan for (M, N, K) on the current device, written to *plan.
+ * Returns a status code. */
 int gemm_f32_plan(int M, int N, int K, gemm_plan_t *plan);
+
+/* The planner's plan for (M, N, K) on a device of num_cus compute units
+ * (num_cus >= 1; GEMM_ERR_INVALID_DIM otherwise): the rounds of tiles it
+ * costs, and a split tail's whole rounds, are num_cus tiles each. For
+ * planning ahead for another device, and for tests. */
+int gemm_f32_plan_cus(int M, int N, int K, int num_cus, gemm_plan_t *plan);
 
 /* Workspace bytes an explicit plan needs (0 for an invalid plan or dims). Only
  * plan->kernel, plan->split_k and plan->split_tail are read. */
@@ -175,12 +201,15 @@ int gemm_f32_with_plan(const float *A, const float *B, float *C, int M, int N, i
  * BLAS conventions: beta == 0 means C is not read (NaN there does not
  * propagate); alpha == 0 or K == 0 means A and B are not read (and may be
  * null) and C <- beta * C (+0.0 when beta == 0). The sum is in FP32 as for
- * gemm_f32; then alpha * sum + beta * c is one FP32 fused multiply-add.
- * alpha = 1, beta = 0, no transposes and dense strides give bit-for-bit the
- * result of gemm_f32 with the same plan.
+ * gemm_f32; then each output is fmaf(alpha, sum, fl(beta * c)): beta * c is
+ * rounded to FP32 on its own and then added by one fused multiply-add (two
+ * roundings in all), or fl(alpha * sum) when beta == 0. alpha = 1, beta = 0,
+ * no transposes and dense strides give bit-for-bit the result of gemm_f32
+ * with the same plan.
  *
- * workspace: null to use the library's per-device split-K workspace (as
- * gemm_f32), else a caller-owned buffer of at least
+ * workspace: null to use the library's split-K workspace (as gemm_f32; not
+ * while the stream captures a graph when the plan splits K:
+ * GEMM_ERR_CAPTURING), else a caller-owned buffer of at least
  * gemm_f32_general_workspace_bytes(...) bytes (GEMM_ERR_WORKSPACE if
  * smaller). A, B, C overlapping: C's extent (first to last element) must not
  * overlap A's or B's (GEMM_ERR_ALIAS). Operands whose rows are so long that

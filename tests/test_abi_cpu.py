@@ -249,3 +249,68 @@ def test_binding_kernel_ids_mirror_the_header():
                                                       if n != "GEMM_KERNEL_AUTO")
     names = [binding.gemm_kernel_name(k) for k in binding.KERNELS.values()]
     assert len(set(names)) == len(names)
+
+
+def test_plans_follow_the_compute_unit_count():
+    """The planner costs rounds of one tile per compute unit. Without a device
+    (this host) gemm_f32_plan plans for 256; a device with another count gets
+    plans made for its own rounds."""
+    for (M, N, K) in [(1536, 1536, 1536), (4096, 4096, 4096), (512, 512, 131072),
+                      (1001, 777, 513), (3000, 3000, 3000)]:
+        a, b = binding.gemm_f32_plan(M, N, K), binding.gemm_f32_plan_cus(M, N, K, 256)
+        assert (a.kernel, a.split_k, a.k_chunk, a.split_tail) == \
+            (b.kernel, b.split_k, b.k_chunk, b.split_tail)
+    # 576 tiles of 64 x 64: 2 rounds + 64 tiles at 256 CUs (split tail),
+    # exactly 3 rounds at 192 (nothing split)
+    p = binding.gemm_f32_plan_cus(1536, 1536, 1536, 256)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_tail == 1 and p.split_k == 2
+    p = binding.gemm_f32_plan_cus(1536, 1536, 1536, 192)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_tail == 0 and p.split_k == 1
+    # 256 tiles of 256 x 256: one round at 256 CUs, two whole rounds at 128
+    for cus in (256, 128):
+        p = binding.gemm_f32_plan_cus(4096, 4096, 4096, cus)
+        assert p.kernel == binding.GEMM_KERNEL_DMA32_256x256_W8_S3 and p.split_k == 1
+    # the long-K product splits K to fill the CUs: fewer CUs, fewer ranges
+    assert binding.gemm_f32_plan_cus(512, 512, 131072, 32).split_k < \
+        binding.gemm_f32_plan_cus(512, 512, 131072, 256).split_k
+    plan = binding.gemm_plan_t()
+    assert binding.raw_status("gemm_f32_plan_cus", 64, 64, 64, 0, ctypes.byref(plan)) == \
+        binding.GEMM_ERR_INVALID_DIM
+    assert binding.raw_status("gemm_f32_plan_cus", 64, 64, 64, 8, None) == binding.GEMM_ERR_NULL_PTR
+
+
+def test_capturing_status_has_its_own_text():
+    text = binding.gemm_status_string(binding.GEMM_ERR_CAPTURING)
+    assert "capturing" in text and text != binding.gemm_status_string(99)
+
+
+REMARKS = """\
+gemm_kernels.hpp:191:1: remark: Function Name: _ZN4gemm1aEv [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:191:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:191:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:191:1: remark:     ScratchSize [bytes/lane]: 40 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:191:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:191:1: remark:     VGPRs Spill: 9 [-Rpass-analysis=kernel-resource-usage]
+  191 | void a() {
+gemm_kernels.hpp:200:1: remark: Function Name: _ZN4gemm1bEv [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:200:1: remark:     VGPRs: 208 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:200:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:200:1: remark:     SGPRs Spill: 33 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:200:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:210:1: remark: Function Name: _ZN4gemm1cEv [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:210:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]
+gemm_kernels.hpp:210:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]
+"""
+
+
+def test_build_refuses_kernels_that_use_scratch_memory():
+    """The build reads the compiler's per-kernel resource report: a kernel with
+    scratch memory or spilled VGPRs fails it; SGPRs spilled into VGPR lanes
+    (no memory) do not."""
+    res = build.kernel_resources(REMARKS)
+    assert set(res) == {"_ZN4gemm1aEv", "_ZN4gemm1bEv", "_ZN4gemm1cEv"}
+    assert res["_ZN4gemm1aEv"]["ScratchSize [bytes/lane]"] == 40
+    assert res["_ZN4gemm1bEv"]["SGPRs Spill"] == 33
+    assert set(build.spilling_kernels(res)) == {"_ZN4gemm1aEv"}
+    assert build.RESOURCE_REMARKS in build.build.__code__.co_consts or \
+        "RESOURCE_REMARKS" in build.build.__code__.co_names

@@ -42,3 +42,29 @@ def test_shader_clock_table(tmp_path, text, want):
     p.write_text(text)
     assert bench.read_sclk(str(p)) == want
     assert bench.read_sclk(str(tmp_path / "absent")) == (None, None)
+
+
+def test_cpu_sample_covers_every_row_when_time_allows():
+    """The CPU baseline's slab is all of C when the oracle's calibrated rate
+    finishes it within the bound (the five standing workloads on the box), so
+    the ragged last tile row of 1001 x 513 x 777 is compared too; otherwise a
+    bounded number of rows, at least one."""
+    assert bench.cpu_sample_rows(1001, 1e4, 12.0) == 1001
+    assert bench.cpu_sample_rows(4096, 4096 / 2.0, 12.0) == 4096
+    assert bench.cpu_sample_rows(4096, 100.0, 12.0) == 1200
+    assert bench.cpu_sample_rows(4096, 1e-3, 12.0) == 1
+
+
+def test_settle_runs_steps_until_the_wall_time_has_passed():
+    calls = []
+    syncs = []
+    el, n = bench.settle(lambda: calls.append(1), lambda: syncs.append(1), 5.0)
+    assert el >= 5.0 and n == len(calls) >= 1
+    # doubling batches, each ended by a synchronisation
+    assert len(syncs) >= 1 and n == 2 ** len(syncs) - 1 or n >= 4096
+
+
+def test_shapes_parse_as_m_k_n():
+    assert bench.parse_shape("1001x513x777") == (1001, 513, 777)
+    assert all(len(bench.parse_shape(s)) == 3 for s in bench.SWEEP_SHAPES + bench.ORDER_SHAPES)
+    assert bench.LADDER_SHAPES == ["1024x512x1024", "1001x513x777"]

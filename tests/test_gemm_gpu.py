@@ -49,9 +49,10 @@ def test_workload_small_integers_bit_exact(w):
 
 
 @pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
-def test_workload_full_size_sampled(w):
-    """Full size, planner's plan: sampled outputs against the oracle one by one,
-    every output finite, and a rerun bit-identical (fixed split-K order)."""
+def test_workload_full_size_every_element(w):
+    """Full size, planner's plan (the launch configuration the bench times):
+    every output against the oracle's full product, and a rerun bit-identical
+    (fixed split-K order)."""
     t = torch()
     say(f"workload {w.name} plan {binding.gemm_f32_plan(w.M, w.N, w.K)}")
     A, B = gemm_inputs.draw_workload(w)
@@ -61,25 +62,24 @@ def test_workload_full_size_sampled(w):
     binding.gemm_f32(dA, dB, dC, w.M, w.N, w.K, s.cuda_stream)
     s.synchronize()
     C = dC.cpu().numpy().reshape(w.M, w.N)
-    assert np.isfinite(C).all()
-    rows, cols = gemm_inputs.sample_indices(w.M, w.N, 3000, seed=w.seed)
-    ref, S = oracle.gemm_entries(A, B, rows, cols)
-    assert_within_bound(C[rows, cols], ref, S, w.name)
     dC2 = nan_buffer(w.M * w.N)
     binding.gemm_f32(dA, dB, dC2, w.M, w.N, w.K, s.cuda_stream)
     s.synchronize()
     assert t.equal(dC.view(t.int32), dC2.view(t.int32))
+    del dA, dB, dC, dC2
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, w.name)
 
 
 @pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
-def test_workload_full_size_integers_sampled(w):
-    say(f"workload {w.name} (integers, sampled)")
+def test_workload_full_size_integers_bit_exact(w):
+    """Full size on small-integer inputs: every output equal in bits to the
+    exact integer product."""
+    say(f"workload {w.name} (integers, every element)")
     A, B = gemm_inputs.draw_workload(w, integer=True)
     C = run(A, B)
-    rows, cols = gemm_inputs.sample_indices(w.M, w.N, 3000, seed=w.seed + 100)
-    ref, _ = oracle.gemm_entries(A, B, rows, cols)
-    assert_bits_equal(C[rows, cols], ref, w.name + " int")
-    assert np.all(C == np.round(C)) and np.abs(C).max() <= 2 ** 24
+    C_ref = oracle.gemm_i64(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    assert_bits_equal(C, C_ref, w.name + " int")
 
 
 # ---------------------------------------------------------------------------
@@ -361,9 +361,8 @@ def test_caller_workspace_matches_library_workspace():
     C1 = run(A, B)
     C2 = run(A, B, entry="gemm_f32_ex")
     assert_bits_equal(C1, C2, "ex vs library workspace")
-    rows, cols = gemm_inputs.sample_indices(M, N, 500)
-    ref, S = oracle.gemm_entries(A, B, rows, cols)
-    assert_within_bound(C1[rows, cols], ref, S, "split-K")
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C1, C_ref, S, "split-K")
 
 
 def test_splitk_deterministic_and_matches_unsplit_on_integers():
@@ -402,14 +401,13 @@ def test_operand_past_2gib_offsets():
     offsets past 2^31 bytes, so such a plan runs the register-staged kernel
     of the same tile (here for the 256 x 256 and the 128 x 64 copy-fed
     kernels); the planner's own plan (split K) and the general form (K passes
-    if needed) run copy-fed. All against sampled oracle entries."""
+    if needed) run copy-fed. Every output against the oracle."""
     t = torch()
     M, K, N = 256, 32768, 16384
     say(f"2 GiB operand {M}x{K}x{N}")
     A, B = gemm_inputs.draw(M, K, N, "normal", seed=99)
     dA, dB = to_dev(A), to_dev(B)
-    rows, cols = gemm_inputs.sample_indices(M, N, 2000, seed=5)
-    ref, S = oracle.gemm_entries(A, B, rows, cols)
+    ref, S = oracle.gemm(A, B)
     del B
     s = t.cuda.current_stream()
     outs = {}
@@ -429,8 +427,7 @@ def test_operand_past_2gib_offsets():
     s.synchronize()
     outs["general"] = dC.cpu().numpy().reshape(M, N)
     for name, C in outs.items():
-        assert np.isfinite(C).all(), name
-        assert_within_bound(C[rows, cols], ref, S, name)
+        assert_within_bound(C, ref, S, name)
 
 
 # ---------------------------------------------------------------------------

@@ -68,3 +68,55 @@ def test_graph_replays_match_eager(M, K, N, form):
         t.cuda.synchronize()
         assert t.equal(dC.view(t.int32), eager.view(t.int32)), f"replay {r}"
         assert t.isfinite(dC).all()
+
+
+def test_library_workspace_refused_under_capture():
+    """gemm_f32 with a plan that splits K needs the library's workspace, whose
+    bookkeeping has no meaning inside a graph: under capture the call returns
+    GEMM_ERR_CAPTURING and enqueues nothing. An unsplit plan needs no
+    workspace and captures and replays like the other entry points."""
+    t = torch()
+    say("graph capture: gemm_f32 split plan refused, unsplit plan captured")
+    Ms, Ks, Ns = 256, 8192, 256
+    assert binding.gemm_f32_plan(Ms, Ns, Ks).split_k > 1
+    X, Y = gemm_inputs.draw(Ms, Ks, Ns, "uniform", seed=7)
+    dA, dB = to_dev(X), to_dev(Y)
+    dC = t.full((Ms, Ns), float("nan"), dtype=t.float32, device="cuda:0")
+    M, K, N = 1001, 513, 777
+    assert binding.gemm_f32_plan(M, N, K).split_k == 1
+    X2, Y2 = gemm_inputs.draw(M, K, N, "uniform", seed=8)
+    dA2, dB2 = to_dev(X2), to_dev(Y2)
+    dC2 = t.empty((M, N), dtype=t.float32, device="cuda:0")
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        binding.gemm_f32(dA2, dB2, dC2, M, N, K, side.cuda_stream)   # warm-up outside capture
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+
+    statuses = []
+    graph = t.cuda.CUDAGraph()
+    with t.cuda.graph(graph):
+        h = t.cuda.current_stream().cuda_stream
+        try:
+            binding.gemm_f32(dA, dB, dC, Ms, Ns, Ks, h)
+            statuses.append(binding.GEMM_OK)
+        except binding.GemmError as e:
+            statuses.append(e.status)
+        binding.gemm_f32(dA2, dB2, dC2, M, N, K, h)
+    t.cuda.synchronize()
+    assert statuses == [binding.GEMM_ERR_CAPTURING]
+    assert t.isnan(dC).all(), "the refused call wrote C"
+    # the refused call works eagerly
+    binding.gemm_f32(dA, dB, dC, Ms, Ns, Ks, t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    assert t.isfinite(dC).all()
+    for r in range(3):
+        dA2.mul_(-0.5)
+        binding.gemm_f32(dA2, dB2, dC2, M, N, K, t.cuda.current_stream().cuda_stream)
+        t.cuda.synchronize()
+        eager = dC2.clone()
+        dC2.fill_(float("nan"))
+        graph.replay()
+        t.cuda.synchronize()
+        assert t.equal(dC2.view(t.int32), eager.view(t.int32)), f"replay {r}"
