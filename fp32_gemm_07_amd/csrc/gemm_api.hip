@@ -121,6 +121,12 @@ bool resolve(int M, int N, int K, int kernel, int split_req, bool split_tail, in
   return out->workgroups() <= INT_MAX;
 }
 
+// The tile order of a launch, its divisors prepared for the device.
+gemm::TileOrder tile_order(const Resolved &r) {
+  return gemm::make_tile_order(static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n), r.splits,
+                               static_cast<int>(r.dp_tiles));
+}
+
 size_t workspace_for(int M, int N, const Resolved &r) {
   return r.splits > 1 ? sizeof(float) * (size_t)r.splits * (size_t)M * (size_t)N : 0;
 }
@@ -417,8 +423,7 @@ void launch_dma_t(const Problem &p, float *ws, const Resolved &r, long long slab
   hipLaunchKernelGGL(
       (gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE, A_KM, B_KM>), grid,
       dim3(64 * WAVES_M * WAVES_N), 0, stream, p.A, p.B, p.C, ws, p.M, p.N, p.K, p.lda, p.ldb,
-      p.ldc, p.alpha, p.beta, r.k_chunk, static_cast<int>(r.tiles_m), static_cast<int>(r.tiles_n),
-      r.splits, static_cast<int>(r.dp_tiles), slab);
+      p.ldc, p.alpha, p.beta, r.k_chunk, tile_order(r), slab);
 }
 
 // ALL_ORDERS: the configuration is built for transposed operands too (the
@@ -594,14 +599,13 @@ int launch(const Problem &p, const Resolved &r, void *workspace, int cus, hipStr
       const long long per_tile = (long long)bm * (v4 ? bn / 4 : bn);
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n - r.dp_tiles),
                       static_cast<unsigned>(ceil_div(per_tile, 4 * gemm::kThreads)));
-      const int tm = static_cast<int>(r.tiles_m), tn = static_cast<int>(r.tiles_n);
-      const int dp = static_cast<int>(r.dp_tiles);
+      const gemm::TileOrder order = tile_order(r);
       if (v4)
         hipLaunchKernelGGL(gemm::tail_reduce_kernel<4>, grid, dim3(gemm::kThreads), 0, stream, ws,
-                           p.C, p.M, p.N, p.ldc, tm, tn, dp, bm, bn, r.splits, p.alpha, p.beta);
+                           p.C, p.M, p.N, p.ldc, order, bm, bn, p.alpha, p.beta);
       else
         hipLaunchKernelGGL(gemm::tail_reduce_kernel<1>, grid, dim3(gemm::kThreads), 0, stream, ws,
-                           p.C, p.M, p.N, p.ldc, tm, tn, dp, bm, bn, r.splits, p.alpha, p.beta);
+                           p.C, p.M, p.N, p.ldc, order, bm, bn, p.alpha, p.beta);
       e = hipGetLastError();
       return e == hipSuccess ? GEMM_OK : hip_fail(e);
     }

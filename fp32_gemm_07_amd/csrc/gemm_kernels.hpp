@@ -46,8 +46,9 @@ struct TileCoord {
 // and each XCD has its own L2. This renumbering of ids 0 .. total-1 gives
 // each XCD one contiguous range of logical ids (a bijection for any count).
 __device__ inline int xcd_order(int bid, int total) {
-  const int q = total / kXcds, r = total % kXcds;
-  const int xcd = bid % kXcds, local = bid / kXcds;
+  const unsigned ut = static_cast<unsigned>(total), ub = static_cast<unsigned>(bid);
+  const int q = static_cast<int>(ut / kXcds), r = static_cast<int>(ut % kXcds);
+  const int xcd = static_cast<int>(ub % kXcds), local = static_cast<int>(ub / kXcds);
   return xcd * q + (xcd < r ? xcd : r) + local;
 }
 
@@ -64,6 +65,62 @@ __device__ inline void grouped_tile(int t, int tiles_m, int tiles_n, int group_m
   const int within = t - g * per_group;
   *tm = first_m + within % gsize;
   *tn = within / gsize;
+}
+
+// Division by a divisor fixed for a launch, without the ~30-instruction
+// integer division sequence: for 1 <= d < 2^31, with s = ceil(log2 d) and
+// m = ceil(2^(31+s) / d) (below 2^32), floor(n / d) = (n * m) >> (31 + s) for
+// every 0 <= n < 2^31. Writing m*d = 2^(31+s) + e with 0 <= e < d,
+// n * m / 2^(31+s) = n / d + n*e / (d * 2^(31+s)), and the second term is
+// below 2^-s <= 1/d, too little to reach the next integer. The host computes
+// m and s once per launch (make_fast_div).
+struct FastDiv {
+  unsigned mul;
+  unsigned shift;   // 31 + s
+};
+
+inline FastDiv make_fast_div(int d) {
+  unsigned s = 0;
+  while ((1LL << s) < d) ++s;
+  const unsigned long long p = 1ULL << (31 + s);
+  return FastDiv{static_cast<unsigned>((p + static_cast<unsigned>(d) - 1) / static_cast<unsigned>(d)),
+                 31 + s};
+}
+
+__device__ inline int fast_div(int n, const FastDiv &d) {
+  return static_cast<int>((static_cast<unsigned long long>(static_cast<unsigned>(n)) * d.mul) >>
+                          d.shift);
+}
+
+// The tile order of one launch, with its divisors prepared on the host
+// (map_tile_fast, grouped_tile_fast: the same mapping as map_tile and
+// grouped_tile below, which divide at run time).
+struct TileOrder {
+  int tiles_m, tiles_n, splits, dp_tiles;
+  FastDiv per_group;   // kGroupM * tiles_n tiles per group of tile rows
+  FastDiv last_rows;   // tile rows of the last group (kGroupM when it is whole)
+  FastDiv tail;        // tiles after the first dp_tiles (the split ones)
+};
+
+inline TileOrder make_tile_order(int tiles_m, int tiles_n, int splits, int dp_tiles) {
+  const int last = tiles_m % kGroupM;
+  const int tail = tiles_m * tiles_n - dp_tiles;
+  return TileOrder{tiles_m, tiles_n, splits, dp_tiles, make_fast_div(kGroupM * tiles_n),
+                   make_fast_div(last ? last : kGroupM), make_fast_div(tail > 0 ? tail : 1)};
+}
+
+__device__ inline void grouped_tile_fast(int t, const TileOrder &o, int *tm, int *tn) {
+  const int g = fast_div(t, o.per_group);
+  const int first_m = g * kGroupM;
+  const int within = t - g * (kGroupM * o.tiles_n);
+  if (o.tiles_m - first_m >= kGroupM) {
+    *tm = first_m + within % kGroupM;
+    *tn = within / kGroupM;
+  } else {
+    const int q = fast_div(within, o.last_rows);
+    *tm = first_m + (within - q * (o.tiles_m - first_m));
+    *tn = q;
+  }
 }
 
 // Workgroup id -> (tile row, tile column, K range).
@@ -90,6 +147,25 @@ __device__ inline TileCoord map_tile(int bid, int tiles_m, int tiles_n, int spli
     c.whole = splits == 1;
   }
   grouped_tile(t, tiles_m, tiles_n, group_m, &c.tm, &c.tn);
+  return c;
+}
+
+// map_tile with group_m = kGroupM and the divisors of a TileOrder.
+__device__ inline TileCoord map_tile_fast(int bid, const TileOrder &o) {
+  TileCoord c;
+  int t;
+  if (bid < o.dp_tiles) {
+    t = xcd_order(bid, o.dp_tiles);
+    c.split = 0;
+    c.whole = 1;
+  } else {
+    const int tail = o.tiles_m * o.tiles_n - o.dp_tiles;
+    const int id = xcd_order(bid - o.dp_tiles, tail * o.splits);
+    c.split = o.splits == 1 ? 0 : fast_div(id, o.tail);
+    t = o.dp_tiles + (id - c.split * tail);
+    c.whole = o.splits == 1;
+  }
+  grouped_tile_fast(t, o, &c.tm, &c.tn);
   return c;
 }
 
@@ -671,7 +747,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
 void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
                           float *__restrict__ C, float *__restrict__ ws, int M, int N, int K,
                           int lda, int ldb, int ldc, float alpha, float beta, int k_chunk,
-                          int tiles_m, int tiles_n, int splits, int dp_tiles, long long slab) {
+                          TileOrder order, long long slab) {
   using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, VEC, A_KMAJOR, B_KMAJOR>;
   using OpA = typename S::OpA;
   using OpB = typename S::OpB;
@@ -680,16 +756,22 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   constexpr int FM = S::FM, FN = S::FN, NG = S::NG, LPW = S::LPW;
   constexpr int STAGE_F = S::STAGE_BYTES / 4;
 
-  __shared__ __attribute__((aligned(16))) float smem[NS * STAGE_F];
-  // One real store into the shared array, so the compiler cannot treat it as
-  // never written (the copies write it behind the compiler's back).
-  if (threadIdx.x == 0) smem[0] = 0.0f;
+  // The stages, then one float of padding that no copy writes: a real store
+  // into it keeps the compiler from treating the array as never written (the
+  // copies write it behind the compiler's back), and since no copy lands
+  // there it needs no ordering against them.
+  __shared__ __attribute__((aligned(16))) float smem[NS * STAGE_F + 4];
+  if (threadIdx.x == 0) smem[NS * STAGE_F] = 0.0f;
+  // The operand pointers are needed only after the tile arithmetic; asking
+  // for them here issues their kernel-argument loads with the others, one
+  // round trip instead of two on the way to the first copy.
+  asm volatile("" : : "s"(A), "s"(B));
 
   // The tile coordinates are uniform; readfirstlane says so to the compiler,
-  // which otherwise keeps the results of the integer divisions of map_tile
-  // in vector registers and everything derived from them (the buffer
-  // resources, the copy bases) with them.
-  const TileCoord tc = map_tile(blockIdx.x, tiles_m, tiles_n, splits, kGroupM, dp_tiles);
+  // which otherwise keeps the results of map_tile in vector registers and
+  // everything derived from them (the buffer resources, the copy bases) with
+  // them.
+  const TileCoord tc = map_tile_fast(blockIdx.x, order);
   const int m0 = __builtin_amdgcn_readfirstlane(tc.tm) * BM;
   const int n0 = __builtin_amdgcn_readfirstlane(tc.tn) * BN;
   const int split = __builtin_amdgcn_readfirstlane(tc.split);
@@ -828,7 +910,6 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // steps t+2 .. t+NS-1 in flight.
   //
   // Prologue: all NS stages issued, step 0 landed, its first fragments.
-  barrier();  // the store into smem[0] precedes every copy
 #pragma unroll
   for (int s = 0; s < NS; ++s)
     if (s < nk) issue_checked(s, smem_base + static_cast<unsigned>(s * S::STAGE_BYTES));
@@ -871,6 +952,17 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
     }
   };
+  // In the last step of the K range only kr_last elements (1 .. BK) are
+  // real; instruction s of a step (4 * group + j) takes k = q*KS + s for lane
+  // group q, so from s = kr_last on it would only add the zero fill: skipped,
+  // and so are fragment reads that only such instructions would use. (A
+  // zero-fill product adds +0.0, which leaves an accumulator's bits as they
+  // are: it starts at +0.0 and never becomes -0.0.)
+  const int kr_last = k_end - (k_begin + (nk - 1) * BK);
+  auto mfma_k = [&](int slot, int g, int j, bool final_step) {
+    if (!final_step || 4 * g + j < kr_last) mfma_step(slot, j);
+  };
+
   // The last R steps of the K range, t0 .. t0+R-1 (t0 a multiple of NS, so
   // step t0+J uses stage J % NS and, when NG is odd, fragment slots of
   // parity J): everything the main loop knows at compile time is known here
@@ -888,12 +980,12 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     for (int g = 0; g < NG; ++g) {
       const int slot = ((J & 1) * NG + g) & 1;
       if (g < NG - 1) {
-        mfma_step(slot, 0);
+        mfma_k(slot, g, 0, !kMore);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(st, g + 1, slot ^ 1);
+        if (kMore || 4 * (g + 1) < kr_last) load_frags(st, g + 1, slot ^ 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        for (int j = 1; j < 4; ++j) mfma_k(slot, g, j, !kMore);
         __builtin_amdgcn_sched_barrier(0);
       } else {
         if constexpr (kMore) {
@@ -902,14 +994,14 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
           barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(slot, 0);
+        mfma_k(slot, g, 0, !kMore);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMore) load_frags(smem + ((ST + 1) % NS) * STAGE_F, 0, slot ^ 1);
         if constexpr (kIssue)
           issue_checked(t0 + J + NS, smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        for (int j = 1; j < 4; ++j) mfma_k(slot, g, j, !kMore);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -925,12 +1017,12 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     for (int g = 0; g < NG; ++g) {
       const int slot = (P * NG + g) & 1;
       if (g < NG - 1) {
-        mfma_step(slot, 0);
+        mfma_k(slot, g, 0, !more);
         __builtin_amdgcn_sched_barrier(0);
-        load_frags(st, g + 1, slot ^ 1);
+        if (more || 4 * (g + 1) < kr_last) load_frags(st, g + 1, slot ^ 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        for (int j = 1; j < 4; ++j) mfma_k(slot, g, j, !more);
         __builtin_amdgcn_sched_barrier(0);
       } else {
         // Steps up to min(nk-1, t+NS-1) have been issued; step t+1 must
@@ -941,14 +1033,14 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
           barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step(slot, 0);
+        mfma_k(slot, g, 0, !more);
         __builtin_amdgcn_sched_barrier(0);
         if (more) load_frags(smem + ((t + 1) % NS) * STAGE_F, 0, slot ^ 1);
         if (t + NS < nk)
           issue_checked(t + NS, smem_base + static_cast<unsigned>(((t + NS) % NS) * S::STAGE_BYTES));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 1; j < 4; ++j) mfma_step(slot, j);
+        for (int j = 1; j < 4; ++j) mfma_k(slot, g, j, !more);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -985,10 +1077,11 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   }
 
   // Epilogue: accumulator v of block (fm, fn) is output row Op::row(q, v) and
-  // column li of that block. The branches on beta and on whether the tile
-  // lies wholly inside C are uniform and taken once: interior tiles store
-  // without per-element checks, and with beta != 0 the C values of a block
-  // row are all loaded before any is used, so their latencies overlap.
+  // column li of that block. With beta != 0 the C values of a block row are
+  // all loaded before any is used, so their latencies overlap. store_tile
+  // (for outputs whose rows are too far apart for the buffer form below):
+  // the branches on beta and on whether the tile lies wholly inside C are
+  // uniform and taken once; interior tiles store without per-element checks.
   auto store_tile = [&](auto beta_is_zero, auto checked) {
     constexpr bool kBetaZero = decltype(beta_is_zero)::value;
     constexpr bool kChecked = decltype(checked)::value;
@@ -1024,7 +1117,73 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
     }
   };
+  // Edge tiles: the same stores through a buffer resource over the output,
+  // from the tile's first element to the last element of C (or of the slab):
+  // the hardware drops a store whose offset lies past the range (and a load
+  // there reads 0), which is where every row at or below M lands, since
+  // offsets grow by ldo >= N per row; lanes whose column lies at or past N
+  // carry kOutOfRange. Straight-line code, without the branch per element of
+  // the checked store_tile (per-wave timestamps on 1001 x 513 x 777: the
+  // slowest edge tile's store 2,148 -> 1,788 clocks). Interior tiles keep
+  // store_tile, whose first store issues sooner (1,072 against 1,440 clocks
+  // for this form). Needs the tile's offsets to fit in 31 bits (BM rows of
+  // ldo floats).
+  auto store_tile_buffer = [&](auto beta_is_zero) {
+    constexpr bool kBetaZero = decltype(beta_is_zero)::value;
+    const long long first = (long long)m0 * ldo + n0;
+    const long long range = 4 * ((long long)(M - 1) * ldo + N - first);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        Cout + first, static_cast<short>(0),
+        static_cast<int>(range < 0x7fffffffLL ? range : 0x7fffffffLL), 0x00020000);
+    unsigned col_off[FN];
+    bool col_ok[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int col = wn * S::WN + OpB::x_of(fn, li);
+      col_ok[fn] = n0 + col < N;
+      col_off[fn] = 4u * static_cast<unsigned>(col);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      unsigned off[FN][S::ACC];
+#pragma unroll
+      for (int v = 0; v < S::ACC; ++v) {
+        const unsigned row_off =
+            4u * static_cast<unsigned>(wm * S::WM + OpA::x_of(fm, Op::row(q, v))) *
+            static_cast<unsigned>(ldo);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) off[fn][v] = col_ok[fn] ? row_off + col_off[fn] : kOutOfRange;
+      }
+      float cv[FN][S::ACC];
+      if constexpr (!kBetaZero) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int v = 0; v < S::ACC; ++v)
+            cv[fn][v] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(off[fn][v]), 0, 0));
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+        for (int v = 0; v < S::ACC; ++v) {
+          float r;
+          if constexpr (kBetaZero)
+            r = alpha_o * acc[fm][fn][v];
+          else
+            r = __builtin_fmaf(alpha_o, acc[fm][fn][v], beta_o * cv[fn][v]);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, r), rc,
+                                                static_cast<int>(off[fn][v]), 0, 0);
+        }
+      }
+    }
+  };
   const bool interior = m0 + BM <= M && n0 + BN <= N;
+  if (!interior && ((long long)BM * ldo + BN) * 4 < (1LL << 31)) {
+    if (beta_o == 0.0f) store_tile_buffer(std::true_type());
+    else store_tile_buffer(std::false_type());
+    return;
+  }
   if (beta_o == 0.0f) {
     if (interior) store_tile(std::true_type(), std::false_type());
     else store_tile(std::true_type(), std::true_type());
@@ -1188,7 +1347,7 @@ void splitk_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, l
 }
 
 // Reduction of a split tail: for each tile after the first dp_tiles of the
-// tile order (map_tile), C <- alpha * sum_s ws[s] + beta * C over its
+// tile order (map_tile_fast), C <- alpha * sum_s ws[s] + beta * C over its
 // elements inside C, the slabs summed in ascending order as above. The slabs
 // are M x N with row stride N; only these tiles' elements are read. Grid:
 // x = tail tile, y = parts of one tile. V = 4 as above (N and ldc multiples
@@ -1196,10 +1355,10 @@ void splitk_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, l
 template <int V>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
 void tail_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, int M, int N, int ldc,
-                        int tiles_m, int tiles_n, int dp_tiles, int bm, int bn, int splits,
-                        float alpha, float beta) {
+                        TileOrder order, int bm, int bn, float alpha, float beta) {
+  const int splits = order.splits;
   int tm, tn;
-  grouped_tile(dp_tiles + blockIdx.x, tiles_m, tiles_n, kGroupM, &tm, &tn);
+  grouped_tile_fast(order.dp_tiles + blockIdx.x, order, &tm, &tn);
   const int m0 = tm * bm, n0 = tn * bn;
   const int rows = min(bm, M - m0), cols = min(bn, N - n0);
   const int per_row = (cols + V - 1) / V;
