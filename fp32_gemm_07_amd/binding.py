@@ -24,6 +24,7 @@ GEMM_ERR_INVALID_PLAN = 5
 GEMM_ERR_HIP = 6
 GEMM_ERR_UNSUPPORTED_DEVICE = 7
 GEMM_ERR_CAPTURING = 8
+GEMM_ERR_SCRATCH_LIMIT = 9
 
 GEMM_KERNEL_AUTO = 0
 GEMM_KERNEL_MFMA_256x256 = 1
@@ -86,7 +87,8 @@ KERNELS = {
 
 # Every symbol include/gemm.h declares.
 EXPORTS = (
-    "gemm_f32", "gemm_f32_workspace_bytes", "gemm_f32_ex", "gemm_f32_plan", "gemm_f32_plan_cus",
+    "gemm_f32", "gemm_f32_noalloc", "gemm_f32_noalloc_scratch_bytes", "gemm_f32_workspace_bytes",
+    "gemm_f32_ex", "gemm_f32_plan", "gemm_f32_plan_cus",
     "gemm_f32_plan_workspace_bytes", "gemm_f32_with_plan", "gemm_f32_general",
     "gemm_f32_general_workspace_bytes", "gemm_kernel_name", "gemm_status_string",
     "gemm_last_hip_error",
@@ -149,6 +151,10 @@ def load():
         plan_p = ctypes.POINTER(gemm_plan_t)
         lib.gemm_f32.argtypes = [vp, vp, vp, i, i, i, vp]
         lib.gemm_f32.restype = i
+        lib.gemm_f32_noalloc.argtypes = [vp, vp, vp, i, i, i, vp]
+        lib.gemm_f32_noalloc.restype = i
+        lib.gemm_f32_noalloc_scratch_bytes.argtypes = []
+        lib.gemm_f32_noalloc_scratch_bytes.restype = sz
         lib.gemm_f32_workspace_bytes.argtypes = [i, i, i]
         lib.gemm_f32_workspace_bytes.restype = sz
         lib.gemm_f32_ex.argtypes = [vp, vp, vp, i, i, i, vp, sz, vp]
@@ -192,6 +198,15 @@ def _check(status: int, where: str) -> int:
 
 def gemm_f32(A, B, C, M: int, N: int, K: int, stream: int = 0) -> None:
     _check(load().gemm_f32(_addr(A), _addr(B), _addr(C), M, N, K, stream or None), "gemm_f32")
+
+
+def gemm_f32_noalloc(A, B, C, M: int, N: int, K: int, stream: int = 0) -> None:
+    _check(load().gemm_f32_noalloc(_addr(A), _addr(B), _addr(C), M, N, K, stream or None),
+           "gemm_f32_noalloc")
+
+
+def gemm_f32_noalloc_scratch_bytes() -> int:
+    return int(load().gemm_f32_noalloc_scratch_bytes())
 
 
 def gemm_f32_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -14,6 +14,15 @@
 #include "gemm_kernels.hpp"
 #include "ladder_kernels.hpp"
 
+// The split-K partial sums of gemm_f32_noalloc: a static device array of
+// kScratchBytes, one copy per device, allocated by the runtime when it loads
+// this code object on the device and held until the process ends. On the
+// host the name `scratch` is only a stand-in for it, not a device address:
+// host code takes each device's address from device_scratch() and passes
+// that to the kernels, never `scratch` itself.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
@@ -297,6 +306,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
   int arch;          // 0 not queried yet, 1 gfx950, -1 another architecture
   int cus;           // multiProcessorCount
+  float *scratch;    // this device's copy of `scratch` (null until first looked up)
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -779,10 +789,26 @@ int with_library_workspace(int dev, size_t need, hipStream_t stream, Body &&body
   return st;
 }
 
+// This device's copy of `scratch` (the no-allocation entry point's split-K
+// buffer), its address looked up once per device with that device current.
+int device_scratch(int dev, float **out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_dev[dev].scratch) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr) return GEMM_ERR_HIP;
+    g_dev[dev].scratch = static_cast<float *>(ptr);
+  }
+  *out = g_dev[dev].scratch;
+  return GEMM_OK;
+}
+
 // Where the split-K partial sums of a plain call go.
 enum class Ws {
   kCaller,    // the caller's buffer (GEMM_ERR_WORKSPACE if too small)
   kLibrary,   // the library's pool (falls back to the unsplit plan if none)
+  kScratch,   // the static `scratch` array (GEMM_ERR_SCRATCH_LIMIT if too small)
 };
 
 // Common path of the plain entry points. `plan_in` null = planner.
@@ -805,12 +831,19 @@ int run(const float *A, const float *B, float *C, int M, int N, int K, const gem
   const size_t need = workspace_for(M, N, r);
   if (mode == Ws::kCaller && need > 0 && (workspace == nullptr || workspace_bytes < need))
     return GEMM_ERR_WORKSPACE;
+  if (mode == Ws::kScratch && need > kScratchBytes) return GEMM_ERR_SCRATCH_LIMIT;
   if (M == 0 || N == 0) return GEMM_OK;
 
   int dev = 0, dev_cus = 0;
   st = check_device(&dev, &dev_cus);
   if (st != GEMM_OK) return st;
   const Problem p = plain_problem(A, B, C, M, N, K);
+  if (mode == Ws::kScratch) {
+    float *scr = nullptr;
+    st = device_scratch(dev, &scr);
+    if (st != GEMM_OK) return st;
+    workspace = scr;
+  }
   if (K == 0) return launch_scale_c(p, cus, stream);
   if (mode == Ws::kLibrary && need > 0) {
     return with_library_workspace(dev, need, stream, [&](void *ws) {
@@ -941,6 +974,13 @@ size_t gemm_f32_workspace_bytes(int M, int N, int K) {
   return workspace_for(M, N, r);
 }
 
+int gemm_f32_noalloc(const float *A, const float *B, float *C, int M, int N, int K,
+                     hipStream_t stream) {
+  return run(A, B, C, M, N, K, nullptr, nullptr, 0, Ws::kScratch, stream);
+}
+
+size_t gemm_f32_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
 int gemm_f32_ex(const float *A, const float *B, float *C, int M, int N, int K, void *workspace,
                 size_t workspace_bytes, hipStream_t stream) {
   return run(A, B, C, M, N, K, nullptr, workspace, workspace_bytes, Ws::kCaller, stream);
@@ -1025,6 +1065,9 @@ const char *gemm_status_string(int status) {
     case GEMM_ERR_CAPTURING:
       return "stream is capturing a graph and the plan needs the library's workspace "
              "(pass a workspace instead)";
+    case GEMM_ERR_SCRATCH_LIMIT:
+      return "the plan's split-K partial sums exceed the static scratch buffer of "
+             "gemm_f32_noalloc (gemm_f32_noalloc_scratch_bytes)";
     default: return "unknown status";
   }
 }

@@ -64,10 +64,12 @@ enum {
   GEMM_ERR_INVALID_PLAN = 5,     /* unknown kernel id, split count < 1 or unusable split_tail */
   GEMM_ERR_HIP = 6,              /* a HIP call failed; see gemm_last_hip_error() */
   GEMM_ERR_UNSUPPORTED_DEVICE = 7, /* the current device is not gfx950 */
-  GEMM_ERR_CAPTURING = 8          /* the stream is capturing a graph and the plan
+  GEMM_ERR_CAPTURING = 8,         /* the stream is capturing a graph and the plan
                                      needs the library-owned workspace (pass a
                                      workspace: gemm_f32_ex, gemm_f32_with_plan,
                                      gemm_f32_general) */
+  GEMM_ERR_SCRATCH_LIMIT = 9      /* gemm_f32_noalloc: the plan's partial sums need
+                                     more than its static scratch buffer */
 };
 
 /* Kernel identifiers for explicit plans. Tile = the BM x BN output block one
@@ -144,6 +146,28 @@ typedef struct gemm_plan {
  * there. Returns a status code. */
 int gemm_f32(const float *A, const float *B, float *C, int M, int N, int K,
              hipStream_t stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. C = A x B
+ * exactly as gemm_f32 computes it (the same plan, so the same bits), with the
+ * split-K partial sums in a static device buffer of
+ * gemm_f32_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on
+ * each device it runs on until the process ends, instead of an allocated
+ * workspace. The call makes no allocation (no hipMalloc, hipFree or
+ * allocating library routine) and no memset: every partial sum is written
+ * before it is read, so nothing needs clearing. Limit: when the plan's
+ * partial sums need more than the buffer (gemm_f32_workspace_bytes(M, N, K) >
+ * gemm_f32_noalloc_scratch_bytes()) the call returns GEMM_ERR_SCRATCH_LIMIT
+ * and enqueues nothing; plans that do not split K need none of it. All calls
+ * on one device share that device's buffer: two such calls whose work
+ * overlaps in time on one device (different streams, or a graph replayed
+ * while another call runs) race and give wrong results; calls ordered on one
+ * stream do not. Returns a status code. */
+int gemm_f32_noalloc(const float *A, const float *B, float *C, int M, int N, int K,
+                     hipStream_t stream);
+
+/* Size in bytes of gemm_f32_noalloc's static scratch buffer. */
+size_t gemm_f32_noalloc_scratch_bytes(void);
 
 /* Bytes of workspace the planner's plan for (M, N, K) needs:
  * 4 * split_k * M * N when it splits K (one M x N slab per K range, also
