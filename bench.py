@@ -55,18 +55,18 @@ DEFAULT_WORKLOAD = "square_4096"
 # (bench.py --copy-probe-mib 256): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
-_SHA = "2445d6074ee3a7d274b9a98ffa51f27fb21796f340f297c12f15673b2220479d"
+_SHA = "0d9329e03ce6184fbef57aa7ef05655368549c898d9128add342f5f754935a9b"
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196738.625, "write_kib": 65536.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 196745.9375, "write_kib": 65536.0, "kernel_source_sha256": _SHA},
     ("longk_512x131072x512", "dma_mfma32_f32_128x128x16_w8_s3"): {
-        "fetch_kib": 262242.5, "write_kib": 16384.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 262244.5, "write_kib": 16384.0, "kernel_source_sha256": _SHA},
     ("regular_1024x512x1024", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 6227.5, "write_kib": 4096.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 6246.0, "write_kib": 4096.0, "kernel_source_sha256": _SHA},
     ("irregular_1001x513x777", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 6293.625, "write_kib": 3147.59375, "kernel_source_sha256": _SHA},
+        "fetch_kib": 6309.875, "write_kib": 3147.59375, "kernel_source_sha256": _SHA},
     ("small_128x96x112", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 140.75, "write_kib": 56.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 151.875, "write_kib": 56.0, "kernel_source_sha256": _SHA},
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
 

@@ -511,7 +511,10 @@ __device__ inline u32x4 make_buffer_rsrc(const void *base, long long bytes) {
   u32x4 r;
   r[0] = static_cast<unsigned>(a);
   r[1] = static_cast<unsigned>(a >> 32) & 0xffffu;  // stride 0: raw byte buffer
-  r[2] = static_cast<unsigned>(bytes < 0 ? 0 : (bytes > 0x80000000LL ? 0x80000000LL : bytes));
+  // The clamp on the bits above 31 (scalar shifts and 32-bit compares; a
+  // 64-bit ordered compare would run on the vector unit).
+  const long long hi = bytes >> 31;
+  r[2] = hi == 0 ? static_cast<unsigned>(bytes) : (static_cast<int>(hi >> 32) < 0 ? 0u : 0x80000000u);
   r[3] = 0x00020000u;                               // 32-bit data, raw access
   return r;
 }
@@ -777,8 +780,21 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   const int split = __builtin_amdgcn_readfirstlane(tc.split);
   const bool whole = __builtin_amdgcn_readfirstlane(tc.whole) != 0;
   const int k_begin = whole ? 0 : split * k_chunk;
-  const int k_end = whole ? K : min(K, k_begin + k_chunk);
-  const int nk = (k_end - k_begin + BK - 1) / BK;
+  const int k_stop = whole ? K : min(K, k_begin + k_chunk);   // end of the K range
+  const int nk_all = (k_stop - k_begin + BK - 1) / BK;
+  // A ragged last K step of at most 4 elements (K = 513 ends one element into
+  // a step) is not staged through LDS: its operands go straight from global
+  // memory into registers, loaded early (reg_step_load) and multiplied after
+  // the ring's last step (reg_step_mfma). Small register tiles only: those
+  // whose last steps are unrolled (a long step hides a stage's cost) and
+  // that have room for the 4 * (FM + FN) registers the operands take. The
+  // ring then runs the whole steps [k_begin, k_end) only.
+  constexpr bool kSmallTile = FM * FN * S::ACC + 8 * (FM + FN) <= 96;
+  constexpr bool kRegStep = FM * FN * S::ACC + 12 * (FM + FN) <= 96;
+  const int kr_tail = k_stop - (k_begin + (nk_all - 1) * BK);
+  const bool reg_step = kRegStep && nk_all >= 2 && kr_tail <= 4;
+  const int nk = reg_step ? nk_all - 1 : nk_all;           // steps through the LDS ring
+  const int k_end = reg_step ? k_stop - kr_tail : k_stop;  // where those steps end
   // Output of this workgroup: C, or its K range's workspace slab.
   float *__restrict__ Cout = whole ? C : ws + (long long)split * slab;
   const int ldo = whole ? ldc : N;
@@ -838,15 +854,16 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
                     stage_byte + S::A_BYTES + opb.lds[i]);
   };
   // Wait until this wave's copies of a step have landed while the copies of
-  // `later` steps issued after it may stay in flight (vmcnt counts this
-  // wave's outstanding copies, oldest first).
-  auto wait_landed = [&](int later) {
+  // `later` steps issued after it, and Y loads issued after those, may stay
+  // in flight (vmcnt counts this wave's outstanding loads, oldest first).
+  auto wait_landed = [&](int later, auto y_c) {
+    constexpr int Y = decltype(y_c)::value;
     if constexpr (NS >= 4) {
-      if (later >= 3) { wait_vmcnt<3 * LPW>(); return; }
+      if (later >= 3) { wait_vmcnt<3 * LPW + Y>(); return; }
     }
-    if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
-    if (later >= 1) { wait_vmcnt<LPW>(); return; }
-    wait_vmcnt<0>();
+    if (later >= 2) { wait_vmcnt<2 * LPW + Y>(); return; }
+    if (later >= 1) { wait_vmcnt<LPW + Y>(); return; }
+    wait_vmcnt<Y>();
   };
   auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
   // When the K range does not end on a 16-byte chunk, the chunk of each
@@ -902,6 +919,65 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
   };
 
+  // The ragged step's operands: instruction s < kr_tail takes k = k_end +
+  // q*KS + s in lane group q, real only in group 0 (kr_tail <= 4 <= KS).
+  // Raw buffer loads through the copies' ranges, only the kr_tail that are
+  // needed per fragment (a uniform count N, dispatched): one lane offset per
+  // fragment, kOutOfRange in the lanes that read zero (group q > 0, rows or
+  // columns outside the matrix: no memory access), and instruction s's k in
+  // the scalar offset. They are issued right after the ring's first copies,
+  // so their latency hides in the wait for step 0, which leaves them in
+  // flight (a wave's loads complete in the order issued).
+  floatx4 ra_reg[FM], rb_reg[FN];
+  auto reg_step_load = [&](auto n_c) {
+    constexpr int N_LOADS = decltype(n_c)::value;
+    // The copies' ranges, in the form the load builtin takes (capped one
+    // byte lower: every valid element ends well below 2^31).
+    auto rsrc = [](const float *base, long long bytes) {
+      const long long hi = bytes >> 31;
+      const int range = hi == 0 ? static_cast<int>(bytes) : (static_cast<int>(hi >> 32) < 0 ? 0 : 0x7fffffff);
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), static_cast<short>(0), range,
+                                               0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t la = rsrc(A + a_first, 4 * (a_end - a_first));
+    const __amdgpu_buffer_rsrc_t lb = rsrc(B + b_first, 4 * (b_end - b_first));
+    const unsigned k0 = static_cast<unsigned>(k_end - k_begin);   // k - k_begin of instruction 0
+    const int a_k = A_KMAJOR ? 4 : 4 * lda;   // bytes from one k to the next
+    const int b_k = B_KMAJOR ? 4 : 4 * ldb;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const unsigned x = static_cast<unsigned>(wm * S::WM + OpA::x_of(fm, li));
+      const unsigned off = A_KMAJOR ? x * static_cast<unsigned>(lda) + k0
+                                    : k0 * static_cast<unsigned>(lda) + x;
+      const int vo = static_cast<int>(q == 0 && m0 + static_cast<int>(x) < M ? 4u * off : kOutOfRange);
+#pragma unroll
+      for (int e = 0; e < N_LOADS; ++e)
+        ra_reg[fm][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(la, vo, e * a_k, 0));
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const unsigned x = static_cast<unsigned>(wn * S::WN + OpB::x_of(fn, li));
+      const unsigned off = B_KMAJOR ? x * static_cast<unsigned>(ldb) + k0
+                                    : k0 * static_cast<unsigned>(ldb) + x;
+      const int vo = static_cast<int>(q == 0 && n0 + static_cast<int>(x) < N ? 4u * off : kOutOfRange);
+#pragma unroll
+      for (int e = 0; e < N_LOADS; ++e)
+        rb_reg[fn][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lb, vo, e * b_k, 0));
+    }
+  };
+  auto reg_step_mfma = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e < kr_tail) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = Op::run(ra_reg[fm][e], rb_reg[fn][e], acc[fm][fn]);
+      }
+    }
+  };
+
   // Schedule. One barrier per K step t, in its last fragment group. Every
   // read of step t's stage was issued before it (the fragments of a step are
   // read during the step before it and the step itself), so right after it
@@ -909,11 +985,32 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // its copies of step t+1 (read from that group on) have landed, leaving
   // steps t+2 .. t+NS-1 in flight.
   //
-  // Prologue: all NS stages issued, step 0 landed, its first fragments.
+  // Prologue: all NS stages issued (no range checks when the ring's first
+  // NS steps are whole and none is the last), step 0 landed, its first
+  // fragments. Issuing every stage up front keeps the later stages' copies in
+  // the shadow of step 0's latency (the copies of a CU's waves share one
+  // address unit; queued behind the barrier they would hold up the first
+  // products).
+  const bool pro_whole = nk > NS;
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (s < nk) issue_checked(s, smem_base + static_cast<unsigned>(s * S::STAGE_BYTES));
-  wait_landed(min(NS, nk) - min(1, nk));
+  for (int s = 0; s < NS; ++s) {
+    const unsigned stage = smem_base + static_cast<unsigned>(s * S::STAGE_BYTES);
+    if (pro_whole) issue_full(s, stage);
+    else if (s < nk) issue_checked(s, stage);
+  }
+  if constexpr (kRegStep) {
+    if (reg_step) {
+      dispatch_count<1, 4>(kr_tail, [&](auto n_c) {
+        reg_step_load(n_c);
+        wait_landed(min(NS, nk) - 1,
+                    std::integral_constant<int, decltype(n_c)::value * (FM + FN)>());
+      });
+    } else {
+      wait_landed(min(NS, nk) - min(1, nk), std::integral_constant<int, 0>());
+    }
+  } else {
+    wait_landed(min(NS, nk) - min(1, nk), std::integral_constant<int, 0>());
+  }
   zero_k_tail(0);
   barrier();
   load_frags(smem, 0, 0);
@@ -959,8 +1056,13 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // zero-fill product adds +0.0, which leaves an accumulator's bits as they
   // are: it starts at +0.0 and never becomes -0.0.)
   const int kr_last = k_end - (k_begin + (nk - 1) * BK);
+  // Whether any instruction of the last step can be skipped: instruction s
+  // is needed while s < kr_last, and a step has KS of them. Otherwise the
+  // last step runs without the per-instruction branches (they cost ~15
+  // clocks each in front of an MFMA).
+  const bool skip_some = kr_last < S::KS;
   auto mfma_k = [&](int slot, int g, int j, bool final_step) {
-    if (!final_step || 4 * g + j < kr_last) mfma_step(slot, j);
+    if (!final_step || !skip_some || 4 * g + j < kr_last) mfma_step(slot, j);
   };
 
   // The last R steps of the K range, t0 .. t0+R-1 (t0 a multiple of NS, so
@@ -997,7 +1099,12 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         mfma_k(slot, g, 0, !kMore);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMore) load_frags(smem + ((ST + 1) % NS) * STAGE_F, 0, slot ^ 1);
-        if constexpr (kIssue)
+        // A copy of a step before the last is of a whole step, as in the
+        // main loop (the advance in soffset, no checks); only the last
+        // step's copies need the range checks.
+        if constexpr (kIssue && J + NS < R - 1)
+          issue_full(t0 + J + NS, smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
+        else if constexpr (kIssue)
           issue_checked(t0 + J + NS, smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1028,7 +1135,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         // Steps up to min(nk-1, t+NS-1) have been issued; step t+1 must
         // have landed.
         if (more) {
-          wait_landed(min(nk - 1, t + NS - 1) - (t + 1));
+          wait_landed(min(nk - 1, t + NS - 1) - (t + 1), std::integral_constant<int, 0>());
           zero_k_tail(t + 1);
           barrier();
         }
@@ -1064,11 +1171,12 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // unrolled copy of the last steps per count. With many accumulators the
   // 2*NS copies make the register allocator spill them, and a long K step
   // hides the looped form's cost, so those keep the loop.
-  constexpr bool kUnrolledTail = FM * FN * S::ACC + 8 * (FM + FN) <= 96;
+  constexpr bool kUnrolledTail = kSmallTile;
   if constexpr (kUnrolledTail) {
     dispatch_count<1, 2 * NS>(nk - t, [&](auto r_c) {
       unroll_steps<0, decltype(r_c)::value>([&](auto j_c) { k_step_last(t, j_c, r_c); });
     });
+    if (reg_step) reg_step_mfma();
   } else {
     for (; t < nk; t += 2) {
       k_step_tail(t, std::integral_constant<int, 0>());

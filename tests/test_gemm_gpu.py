@@ -191,6 +191,42 @@ def test_every_last_step_count(kname, steps, off, split):
     assert_within_bound(C, C_ref, S, f"{kname} K {K} split {split}")
 
 
+# A last step of 1 to 4 elements (K = 513 ends one element into its step):
+# the small-tile copy-fed kernels read it from global memory into registers
+# instead of copying it through the LDS ring; the others stage it as usual.
+# Every ring length from 1 to 2 x stages + 1 before it, float and integer
+# inputs (the integer sums pin which lane takes which k of the extra step).
+
+RAGGED_STEPS = [2, 3, 4, 5, 7, 8, 13]
+
+
+@pytest.mark.parametrize("kname", DMA_KERNELS)
+@pytest.mark.parametrize("steps", RAGGED_STEPS)
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
+@pytest.mark.parametrize("split", [1, 2])
+def test_short_last_step(kname, steps, r, split):
+    K = K_STEP[kname] * (steps - 1) + r
+    M, N = 70, 90
+    say(f"short last step {kname} K {K} ({steps} steps, {r} in the last) split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "uniform", seed=K * 5 + split)
+    C = run(A, B, plan=binding.make_plan(binding.KERNELS[kname], split))
+    C_ref, S = oracle.gemm(A, B)
+    assert_within_bound(C, C_ref, S, f"{kname} K {K} split {split}")
+
+
+@pytest.mark.parametrize("kname", DMA_KERNELS)
+@pytest.mark.parametrize("r", [1, 2, 3, 4])
+@pytest.mark.parametrize("split", [1, 2])
+def test_short_last_step_integers_bit_exact(kname, r, split):
+    K = K_STEP[kname] * 4 + r
+    M, N = 130, 97
+    say(f"short last step {kname} int K {K} split {split}")
+    A, B = gemm_inputs.draw(M, K, N, "int", seed=K + split)
+    C = run(A, B, plan=binding.make_plan(binding.KERNELS[kname], split))
+    C_ref = oracle.gemm_i64(A.astype(np.int64), B.astype(np.int64)).astype(np.float32)
+    assert_bits_equal(C, C_ref, f"{kname} int K {K} split {split}")
+
+
 def test_split_tail_planner_1536():
     """1536^3: the planner splits the last round of 64 tiles of 64 x 64 two
     ways; every output against the oracle, a rerun bit-identical, caller and
