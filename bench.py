@@ -11,7 +11,8 @@ split-K reduce included) on inputs already resident in HBM. First an untimed
 clock-settle pass: the same step back to back for --settle-ms of wall time
 (the chip raises its shader clock over the first ~30 ms of sustained load,
 and launches timed inside that ramp run up to 25 % slower); then W untimed
-warm-up steps; then K timed steps back to back between two device
+warm-up steps; then K timed steps (default: about 20 ms of work at the
+settle pass's rate, at least 100) back to back between two device
 synchronisations (host wall clock: `value`) and between two HIP events on the
 stream they are launched on (device time / K: the mean launch duration of the
 roofline); then a short pass of up to 20 launches, each between its own event
@@ -47,6 +48,9 @@ from fp32_gemm_07_amd import binding, roofline  # noqa: E402
 
 METRIC = "FP32 GEMM TFLOPS (2MNK/s) and % of MI355X FP32 peak, 1 GPU"
 DEFAULT_WORKLOAD = "square_4096"
+# Timed work the default step count aims at (the fixed cost of the two
+# synchronisations around the timed region, ~25 us, then stays below 0.2 %).
+DEFAULT_TIMED_MS = 20.0
 
 # HBM traffic per launch from two rocprofv3 --pmc runs of this bench
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), keyed by (workload, kernel
@@ -55,18 +59,18 @@ DEFAULT_WORKLOAD = "square_4096"
 # (bench.py --copy-probe-mib 256): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
-_SHA = "0d9329e03ce6184fbef57aa7ef05655368549c898d9128add342f5f754935a9b"
+_SHA = "64ba97fd2322ec7dea5c7e92eb1c839377b92d80c7bb541c8947570043d18534"
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196745.9375, "write_kib": 65536.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 196731.75, "write_kib": 65536.0, "kernel_source_sha256": _SHA},
     ("longk_512x131072x512", "dma_mfma32_f32_128x128x16_w8_s3"): {
-        "fetch_kib": 262244.5, "write_kib": 16384.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 262247.0, "write_kib": 16384.0, "kernel_source_sha256": _SHA},
     ("regular_1024x512x1024", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 6246.0, "write_kib": 4096.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 6238.0, "write_kib": 4096.0, "kernel_source_sha256": _SHA},
     ("irregular_1001x513x777", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 6309.875, "write_kib": 3147.59375, "kernel_source_sha256": _SHA},
+        "fetch_kib": 6301.875, "write_kib": 3147.59375, "kernel_source_sha256": _SHA},
     ("small_128x96x112", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 151.875, "write_kib": 56.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 146.75, "write_kib": 56.0, "kernel_source_sha256": _SHA},
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
 
@@ -88,7 +92,9 @@ def measured_traffic(workload: str, kernel: str):
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=None,
+                   help="timed steps (default: about 20 ms of timed work at the settle pass's rate, "
+                        "at least 100)")
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--settle-ms", type=float, default=200.0,
                    help="untimed back-to-back steps for at least this much wall time before the "
@@ -436,7 +442,7 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     if args.copy_probe_mib:
-        return copy_probe(args.copy_probe_mib, args.steps)
+        return copy_probe(args.copy_probe_mib, args.steps or 100)
     if args.sweep is not None:
         return run_sweep(torch, args.sweep or SWEEP_SHAPES, args.settle_ms)
     if args.ladder:
@@ -469,6 +475,9 @@ def main(argv=None):
         binding.gemm_f32_with_plan(dA, dB, dC, M, N, K, plan, ws, ws_bytes, h)
 
     settle_ms, settle_steps = settle(step, torch.cuda.synchronize, args.settle_ms)
+    if args.steps is None:   # the fixed cost around the timed region stays below ~0.2 %
+        per_step_ms = settle_ms / settle_steps if settle_steps else 1.0
+        args.steps = max(100, int(round(DEFAULT_TIMED_MS / per_step_ms)))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

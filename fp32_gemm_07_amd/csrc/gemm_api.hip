@@ -11,6 +11,7 @@
 #include <cmath>
 #include <mutex>
 
+#include "dma_launch.hpp"
 #include "gemm_kernels.hpp"
 #include "ladder_kernels.hpp"
 
@@ -421,43 +422,20 @@ bool launch_mfma(const float *A, const float *B, float *out, int M, int N, int K
 
 // Kernels fed by direct global -> LDS copies (16-byte copies from 4-byte
 // aligned sources, any K, N and row strides, either storage order of each
-// operand). Whole tiles get alpha * op(A) op(B) + beta * C, split ones their
-// K range's partial product in workspace slab s (ws + s * slab, row stride
-// N). Returns false (nothing launched) when the operand offsets of one
-// workgroup would not fit in 32 bits.
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE, bool A_KM,
-          bool B_KM>
-void launch_dma_t(const Problem &p, float *ws, const Resolved &r, long long slab,
-                  hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(r.workgroups()));
-  hipLaunchKernelGGL(
-      (gemm::mfma_dma_gemm_kernel<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, 4, WPE, A_KM, B_KM>), grid,
-      dim3(64 * WAVES_M * WAVES_N), 0, stream, p.A, p.B, p.C, ws, p.M, p.N, p.K, p.lda, p.ldb,
-      p.ldc, p.alpha, p.beta, r.k_chunk, tile_order(r), slab);
-}
-
-// ALL_ORDERS: the configuration is built for transposed operands too (the
-// planner's 256x256, 8-wave 128x128 and 64x64 kernels); the others take
-// op(A) = A, op(B) = B only.
-template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE,
-          bool ALL_ORDERS>
+// operand), launched from their own translation unit (dma_launch.hpp).
+// Whole tiles get alpha * op(A) op(B) + beta * C, split ones their K range's
+// partial product in workspace slab s (ws + s * slab, row stride N). Returns
+// false (nothing launched) when the operand offsets of one workgroup would
+// not fit in 32 bits, or the configuration is not built for the operands'
+// storage order.
 bool launch_dma(const Problem &p, float *ws, const Resolved &r, long long slab,
                 hipStream_t stream) {
-  if (!dma_fits(p, BM, BN, BK, r.k_span())) return false;
-#define LGEMM_DMA(AK, BKM)                                                                  \
-  launch_dma_t<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, WPE, AK, BKM>(p, ws, r, slab, stream)
-  if (!p.ta && !p.tb) {
-    LGEMM_DMA(true, false);
-    return true;
-  }
-  if constexpr (ALL_ORDERS) {
-    if (p.ta && !p.tb) LGEMM_DMA(false, false);
-    else if (!p.ta && p.tb) LGEMM_DMA(true, true);
-    else LGEMM_DMA(false, true);
-    return true;
-  }
-#undef LGEMM_DMA
-  return false;
+  const KernelInfo &k = *r.k;
+  if (!dma_fits(p, k.bm, k.bn, k.bk, r.k_span())) return false;
+  const gemm::DmaLaunch d{p.A,     p.B,      p.C,  ws,   p.M,       p.N,  p.K,
+                          p.lda,   p.ldb,    p.ldc, p.alpha, p.beta, p.ta, p.tb,
+                          r.k_chunk, slab,   gemm::kernel_order(tile_order(r)), r.workgroups()};
+  return gemm::launch_dma_kernel(k.id, d, stream);
 }
 
 // Launch the kernel of r.k for the product or, when r splits K, the partial
@@ -522,43 +500,43 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
       launch_mfma<32, 64, 64, 16, 1, 1, 2, 2>(A, B, out, M, N, K, r, slab, stream);
       return true;
     case GEMM_KERNEL_DMA32_256x256_W8:
-      return launch_dma<32, 256, 256, 16, 2, 4, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
-      return launch_dma<32, 256, 256, 16, 2, 4, 3, 2, true>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 256, 256, 16, 2, 2, 1, 1>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_128x128_W4:
-      return launch_dma<32, 128, 128, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA16_128x128_W4:
-      return launch_dma<16, 128, 128, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA16_64x64:
-      return launch_dma<16, 64, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<16, 64, 64, 32, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA32_64x64:
-      return launch_dma<32, 64, 64, 16, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_DMA16_128x64:
-      return launch_dma<16, 128, 64, 32, 2, 2, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<16, 128, 64, 32, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                    stream));
     case GEMM_KERNEL_DMA32_128x128_W8:
-      return launch_dma<32, 128, 128, 16, 2, 4, 4, 2, false>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_128x128_W8_S3:
-      return launch_dma<32, 128, 128, 16, 2, 4, 3, 2, true>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 128, 128, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                     stream));
     case GEMM_KERNEL_DMA32_64x64_S3:
-      return launch_dma<32, 64, 64, 16, 2, 2, 3, 2, true>(p, ws, r, slab, stream) ||
+      return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
     case GEMM_KERNEL_VALU_64x64: {

@@ -92,21 +92,35 @@ __device__ inline int fast_div(int n, const FastDiv &d) {
                           d.shift);
 }
 
-// The tile order of one launch, with its divisors prepared on the host
-// (map_tile_fast, grouped_tile_fast: the same mapping as map_tile and
-// grouped_tile below, which divide at run time).
+// The tile order of one launch, with the divisors of its grouped order
+// prepared on the host (map_tile_fast, grouped_tile_fast: the same mapping as
+// map_tile and grouped_tile below, which divide at run time).
 struct TileOrder {
   int tiles_m, tiles_n, splits, dp_tiles;
   FastDiv per_group;   // kGroupM * tiles_n tiles per group of tile rows
   FastDiv last_rows;   // tile rows of the last group (kGroupM when it is whole)
-  FastDiv tail;        // tiles after the first dp_tiles (the split ones)
 };
 
 inline TileOrder make_tile_order(int tiles_m, int tiles_n, int splits, int dp_tiles) {
   const int last = tiles_m % kGroupM;
-  const int tail = tiles_m * tiles_n - dp_tiles;
   return TileOrder{tiles_m, tiles_n, splits, dp_tiles, make_fast_div(kGroupM * tiles_n),
-                   make_fast_div(last ? last : kGroupM), make_fast_div(tail > 0 ? tail : 1)};
+                   make_fast_div(last ? last : kGroupM)};
+}
+
+// The copy-fed kernel's scalar form of a tile order. Without a split every
+// tile is whole, and the whole-tile path of map_tile_fast maps workgroup ids
+// exactly as the split path does with one K range (xcd_order over all tiles),
+// so dp_tiles becomes the tile count and that path needs neither the split
+// count nor its divisor.
+struct KernelOrder {
+  int dp_tiles;
+  unsigned group_mul, rows_mul, shifts;
+  int splits;
+};
+
+inline KernelOrder kernel_order(const TileOrder &o) {
+  return KernelOrder{o.splits == 1 ? o.tiles_m * o.tiles_n : o.dp_tiles, o.per_group.mul,
+                     o.last_rows.mul, o.per_group.shift | (o.last_rows.shift << 8), o.splits};
 }
 
 __device__ inline void grouped_tile_fast(int t, const TileOrder &o, int *tm, int *tn) {
@@ -159,9 +173,11 @@ __device__ inline TileCoord map_tile_fast(int bid, const TileOrder &o) {
     c.split = 0;
     c.whole = 1;
   } else {
+    // Split tiles (large products only, where a run-time division costs
+    // nothing that shows).
     const int tail = o.tiles_m * o.tiles_n - o.dp_tiles;
     const int id = xcd_order(bid - o.dp_tiles, tail * o.splits);
-    c.split = o.splits == 1 ? 0 : fast_div(id, o.tail);
+    c.split = o.splits == 1 ? 0 : id / tail;
     t = o.dp_tiles + (id - c.split * tail);
     c.whole = o.splits == 1;
   }
@@ -742,15 +758,26 @@ struct DmaShape {
 // into workspace slab `split` (ws + split * slab, row stride N, written as
 // is). op(A) is K-contiguous when A_KMAJOR (A given M x K), op(B) when
 // B_KMAJOR (B given N x K, i.e. transposed). beta == 0: C is not read.
+//
+// The tile order comes as scalars (its whole-tile count, the multipliers of
+// its divisors by 8 * tiles_n and by the last group's rows, their two shifts
+// packed 8 bits apart, the split count: see kernel_order), and the arguments
+// that the tile order and the first copies need come first: the library is
+// built with the first 12 arguments (14 dwords, the most there is room for)
+// preloaded into scalar registers at wave launch, so the tile order, the
+// address set-up and the first copies do not wait for the kernel-argument
+// read (about 600 clocks, its first access missing every cache); the others
+// arrive meanwhile, needed by the epilogue or on the split path only.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int VEC,
           int WAVES_PER_EU, bool A_KMAJOR, bool B_KMAJOR>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WAVES_M * WAVES_N,
                                                       64 * WAVES_M * WAVES_N),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
-void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B,
-                          float *__restrict__ C, float *__restrict__ ws, int M, int N, int K,
-                          int lda, int ldb, int ldc, float alpha, float beta, int k_chunk,
-                          TileOrder order, long long slab) {
+void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__ B, int M, int N,
+                          int K, int lda, int ldb, int dp_tiles, unsigned group_mul,
+                          unsigned rows_mul, unsigned shifts, int splits, float *__restrict__ C,
+                          float *__restrict__ ws, int ldc, float alpha, float beta, int k_chunk,
+                          long long slab) {
   using S = DmaShape<MI, BM, BN, BK, WAVES_M, WAVES_N, NS, VEC, A_KMAJOR, B_KMAJOR>;
   using OpA = typename S::OpA;
   using OpB = typename S::OpB;
@@ -774,13 +801,27 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // which otherwise keeps the results of map_tile in vector registers and
   // everything derived from them (the buffer resources, the copy bases) with
   // them.
+  TileOrder order;
+  order.tiles_m = static_cast<int>((static_cast<unsigned>(M) + BM - 1) / BM);
+  order.tiles_n = static_cast<int>((static_cast<unsigned>(N) + BN - 1) / BN);
+  order.splits = splits;
+  order.dp_tiles = dp_tiles;
+  order.per_group = FastDiv{group_mul, shifts & 0xffu};
+  order.last_rows = FastDiv{rows_mul, shifts >> 8};
   const TileCoord tc = map_tile_fast(blockIdx.x, order);
   const int m0 = __builtin_amdgcn_readfirstlane(tc.tm) * BM;
   const int n0 = __builtin_amdgcn_readfirstlane(tc.tn) * BN;
   const int split = __builtin_amdgcn_readfirstlane(tc.split);
   const bool whole = __builtin_amdgcn_readfirstlane(tc.whole) != 0;
-  const int k_begin = whole ? 0 : split * k_chunk;
-  const int k_stop = whole ? K : min(K, k_begin + k_chunk);   // end of the K range
+  // The K range. k_chunk is not preloaded; the empty asm keeps the compiler
+  // from computing the split side on every path (as a select), which would
+  // make whole tiles wait for the kernel-argument read.
+  int k_begin = 0, k_stop = K;   // k_stop: end of the K range
+  if (!whole) {
+    asm volatile("" ::: "memory");
+    k_begin = split * k_chunk;
+    k_stop = min(K, k_begin + k_chunk);
+  }
   const int nk_all = (k_stop - k_begin + BK - 1) / BK;
   // A ragged last K step of at most 4 elements (K = 513 ends one element into
   // a step) is not staged through LDS: its operands go straight from global
@@ -795,11 +836,6 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   const bool reg_step = kRegStep && nk_all >= 2 && kr_tail <= 4;
   const int nk = reg_step ? nk_all - 1 : nk_all;           // steps through the LDS ring
   const int k_end = reg_step ? k_stop - kr_tail : k_stop;  // where those steps end
-  // Output of this workgroup: C, or its K range's workspace slab.
-  float *__restrict__ Cout = whole ? C : ws + (long long)split * slab;
-  const int ldo = whole ? ldc : N;
-  const float alpha_o = whole ? alpha : 1.0f;
-  const float beta_o = whole ? beta : 0.0f;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -854,16 +890,15 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
                     stage_byte + S::A_BYTES + opb.lds[i]);
   };
   // Wait until this wave's copies of a step have landed while the copies of
-  // `later` steps issued after it, and Y loads issued after those, may stay
-  // in flight (vmcnt counts this wave's outstanding loads, oldest first).
-  auto wait_landed = [&](int later, auto y_c) {
-    constexpr int Y = decltype(y_c)::value;
+  // `later` steps issued after it may stay in flight (vmcnt counts this
+  // wave's outstanding loads, oldest first).
+  auto wait_landed = [&](int later) {
     if constexpr (NS >= 4) {
-      if (later >= 3) { wait_vmcnt<3 * LPW + Y>(); return; }
+      if (later >= 3) { wait_vmcnt<3 * LPW>(); return; }
     }
-    if (later >= 2) { wait_vmcnt<2 * LPW + Y>(); return; }
-    if (later >= 1) { wait_vmcnt<LPW + Y>(); return; }
-    wait_vmcnt<Y>();
+    if (later >= 2) { wait_vmcnt<2 * LPW>(); return; }
+    if (later >= 1) { wait_vmcnt<LPW>(); return; }
+    wait_vmcnt<0>();
   };
   auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory"); };
   // When the K range does not end on a 16-byte chunk, the chunk of each
@@ -925,9 +960,11 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // needed per fragment (a uniform count N, dispatched): one lane offset per
   // fragment, kOutOfRange in the lanes that read zero (group q > 0, rows or
   // columns outside the matrix: no memory access), and instruction s's k in
-  // the scalar offset. They are issued right after the ring's first copies,
-  // so their latency hides in the wait for step 0, which leaves them in
-  // flight (a wave's loads complete in the order issued).
+  // the scalar offset. They are issued just before the ring's first copies:
+  // issued after them, they would queue behind the CU's prologue copies in
+  // the shared address unit (about 430 clocks); issued before, they cost
+  // their few instructions and complete before step 0 does (a wave's loads
+  // complete in the order issued), so the wait for step 0 covers them.
   floatx4 ra_reg[FM], rb_reg[FN];
   auto reg_step_load = [&](auto n_c) {
     constexpr int N_LOADS = decltype(n_c)::value;
@@ -991,6 +1028,9 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // the shadow of step 0's latency (the copies of a CU's waves share one
   // address unit; queued behind the barrier they would hold up the first
   // products).
+  if constexpr (kRegStep) {
+    if (reg_step) dispatch_count<1, 4>(kr_tail, [&](auto n_c) { reg_step_load(n_c); });
+  }
   const bool pro_whole = nk > NS;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -998,19 +1038,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     if (pro_whole) issue_full(s, stage);
     else if (s < nk) issue_checked(s, stage);
   }
-  if constexpr (kRegStep) {
-    if (reg_step) {
-      dispatch_count<1, 4>(kr_tail, [&](auto n_c) {
-        reg_step_load(n_c);
-        wait_landed(min(NS, nk) - 1,
-                    std::integral_constant<int, decltype(n_c)::value * (FM + FN)>());
-      });
-    } else {
-      wait_landed(min(NS, nk) - min(1, nk), std::integral_constant<int, 0>());
-    }
-  } else {
-    wait_landed(min(NS, nk) - min(1, nk), std::integral_constant<int, 0>());
-  }
+  wait_landed(min(NS, nk) - min(1, nk));
   zero_k_tail(0);
   barrier();
   load_frags(smem, 0, 0);
@@ -1135,7 +1163,7 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         // Steps up to min(nk-1, t+NS-1) have been issued; step t+1 must
         // have landed.
         if (more) {
-          wait_landed(min(nk - 1, t + NS - 1) - (t + 1), std::integral_constant<int, 0>());
+          wait_landed(min(nk - 1, t + NS - 1) - (t + 1));
           zero_k_tail(t + 1);
           barrier();
         }
@@ -1183,6 +1211,18 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       if (t + 1 < nk) k_step_tail(t + 1, std::integral_constant<int, 1>());
     }
   }
+
+  // k_chunk stays live until here: were its register reused after the split
+  // path's last read, the reuse would have to wait for the argument read
+  // that fills it, on every path.
+  asm volatile("" : : "s"(k_chunk));
+  // Output of this workgroup: C, or its K range's workspace slab (the
+  // arguments that say so are not among the preloaded ones: read here, not
+  // before the first copies).
+  float *__restrict__ Cout = whole ? C : ws + (long long)split * slab;
+  const int ldo = whole ? ldc : N;
+  const float alpha_o = whole ? alpha : 1.0f;
+  const float beta_o = whole ? beta : 0.0f;
 
   // Epilogue: accumulator v of block (fm, fn) is output row Op::row(q, v) and
   // column li of that block. With beta != 0 the C values of a block row are
@@ -1499,7 +1539,9 @@ void tail_reduce_kernel(const float *__restrict__ ws, float *__restrict__ C, int
 
 // C <- beta * C over M x N with row stride ldc, +0.0 when beta == 0 (C then
 // not read): the whole result when K = 0 or alpha = 0.
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads)))
+// (static: not a template, and the header is compiled in two translation
+// units; only gemm_api.hip launches it)
+static __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), unused))
 void scale_c_kernel(float *__restrict__ C, long long count, int N, int ldc, float beta) {
   const long long stride = (long long)gridDim.x * kThreads;
   for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < count; e += stride) {
