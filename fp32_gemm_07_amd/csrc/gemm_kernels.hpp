@@ -527,10 +527,21 @@ __device__ inline u32x4 make_buffer_rsrc(const void *base, long long bytes) {
   u32x4 r;
   r[0] = static_cast<unsigned>(a);
   r[1] = static_cast<unsigned>(a >> 32) & 0xffffu;  // stride 0: raw byte buffer
-  // The clamp on the bits above 31 (scalar shifts and 32-bit compares; a
-  // 64-bit ordered compare would run on the vector unit).
-  const long long hi = bytes >> 31;
-  r[2] = hi == 0 ? static_cast<unsigned>(bytes) : (static_cast<int>(hi >> 32) < 0 ? 0u : 0x80000000u);
+  // The clamp in five scalar instructions on the two halves: written in C++,
+  // the compiler turns it into 64-bit ordered compares, which run on the
+  // vector unit and cost several times as many instructions.
+  const unsigned lo = static_cast<unsigned>(bytes);
+  const unsigned hi = static_cast<unsigned>(static_cast<unsigned long long>(bytes) >> 32);
+  unsigned range;
+  asm("s_cmp_lg_u32 %1, 0\n\t"
+      "s_cselect_b32 %0, 0x80000000, %2\n\t"   // high half set: 2^31 or more (or negative)
+      "s_min_u32 %0, %0, 0x80000000\n\t"
+      "s_cmp_lt_i32 %1, 0\n\t"
+      "s_cselect_b32 %0, 0, %0"                   // negative: empty
+      : "=&s"(range)
+      : "s"(hi), "s"(lo)
+      : "scc");
+  r[2] = range;
   r[3] = 0x00020000u;                               // 32-bit data, raw access
   return r;
 }
@@ -964,20 +975,21 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // issued after them, they would queue behind the CU's prologue copies in
   // the shared address unit (about 430 clocks); issued before, they cost
   // their few instructions and complete before step 0 does (a wave's loads
-  // complete in the order issued), so the wait for step 0 covers them.
+  // complete in the order issued), so the wait for step 0 covers them; issued
+  // in the main loop's first step instead, they missed the L2 and held the
+  // next step's wait (the main loop +400 clocks).
   floatx4 ra_reg[FM], rb_reg[FN];
   auto reg_step_load = [&](auto n_c) {
     constexpr int N_LOADS = decltype(n_c)::value;
-    // The copies' ranges, in the form the load builtin takes (capped one
-    // byte lower: every valid element ends well below 2^31).
-    auto rsrc = [](const float *base, long long bytes) {
-      const long long hi = bytes >> 31;
-      const int range = hi == 0 ? static_cast<int>(bytes) : (static_cast<int>(hi >> 32) < 0 ? 0 : 0x7fffffff);
-      return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), static_cast<short>(0), range,
-                                               0x00020000);
+    // The copies' resources, in the form the load builtin takes: same base,
+    // the same range capped one byte lower (every valid element ends well
+    // below 2^31).
+    auto rsrc = [](const float *base, unsigned range) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), static_cast<short>(0),
+                                               static_cast<int>(min(range, 0x7fffffffu)), 0x00020000);
     };
-    const __amdgpu_buffer_rsrc_t la = rsrc(A + a_first, 4 * (a_end - a_first));
-    const __amdgpu_buffer_rsrc_t lb = rsrc(B + b_first, 4 * (b_end - b_first));
+    const __amdgpu_buffer_rsrc_t la = rsrc(A + a_first, ra[2]);
+    const __amdgpu_buffer_rsrc_t lb = rsrc(B + b_first, rb[2]);
     const unsigned k0 = static_cast<unsigned>(k_end - k_begin);   // k - k_begin of instruction 0
     const int a_k = A_KMAJOR ? 4 : 4 * lda;   // bytes from one k to the next
     const int b_k = B_KMAJOR ? 4 : 4 * ldb;
