@@ -55,7 +55,9 @@ bool launch_dma_kernel(int kernel, const DmaLaunch &d, hipStream_t stream) {
     case GEMM_KERNEL_DMA32_64x64:
       return launch_orders<32, 64, 64, 16, 2, 2, 4, 2, false>(d, stream);
     case GEMM_KERNEL_DMA16_128x64:
-      return launch_orders<16, 128, 64, 32, 2, 2, 4, 2, false>(d, stream);
+      // 96 KiB of LDS: one workgroup, so one wave per SIMD, per CU; built for
+      // that (asking for two would only constrain the register allocator)
+      return launch_orders<16, 128, 64, 32, 2, 2, 4, 1, false>(d, stream);
     case GEMM_KERNEL_DMA32_128x128_W8:
       return launch_orders<32, 128, 128, 16, 2, 4, 4, 2, false>(d, stream);
     case GEMM_KERNEL_DMA32_128x128_W8_S3:
