@@ -360,6 +360,7 @@ def run_sweep(torch, shapes, settle_ms: float) -> int:
                         "tflops": round(flop / t_auto / 1e6, 2)},
             "vendor_torch_matmul": {"us": round(t_vendor, 2), "tflops": round(flop / t_vendor / 1e6, 2)},
             "fastest": [{"plan": name, "us": round(us, 2)} for us, name in res[:4]],
+            "all": {name: round(us, 2) for us, name in res},
             "plans_timed": len(res), "reps": reps, "timing": "median of event pairs"}), flush=True)
     return 0
 

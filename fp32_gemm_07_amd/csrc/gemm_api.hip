@@ -239,9 +239,12 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   double rounds = std::ceil(split_tiles * r.splits / cus);
   // The pieces of a split tail start as the whole tiles end, on whichever CU
   // frees a slot first. A CU holds two workgroups of a 4-wave kernel: with
-  // more pieces than half the CUs some CU takes two of them side by side
-  // (measured at 1536^3, 256 pieces: the last ends ~6 us after the rest), so
-  // such a round is costed as two.
+  // more pieces than half the CUs some CU can take two of them side by side,
+  // so such a round is costed as two. How much that costs depends on how the
+  // whole tiles end: 256 pieces of 64 x 64 tiles after two whole rounds take
+  // 66 against 62 us for 128 pieces at 1500^3 (the rule's choice), but 61
+  // against 63.5 us at 1536^3, where the rule picks the 128 (three runs each);
+  // without the rule the two swap, with no gain over the shapes measured.
   if (r.dp_tiles > 0 && c.slots_per_cu > 1 && split_tiles * r.splits > cus / 2)
     rounds = std::max(rounds, 2.0);
   double us = rounds * per_wg + c.fixed_us;
