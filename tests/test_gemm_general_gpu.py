@@ -248,6 +248,44 @@ def test_general_split_tail(ta, tb, pads):
     check(got, ref, S, M, N, ldc, "split tail general")
 
 
+# A last K step of 1 to 4 elements in the planner's plans: the kernels with few
+# accumulators per wave read it into registers instead of staging it in LDS.
+# Shapes whose plans put it in every variant the general form reaches: a
+# 16-way split (last range only), a split tail (the whole tiles and the last
+# range of the split ones), the 8-wave 128 x 128 kernel whole and with a split
+# tail; every storage order, alpha, beta and padded rows.
+SHORT_STEP = [((256, 8193, 256), "dma_mfma32_f32_64x64x16_w4_s3", 16, 0),
+              ((1536, 1540, 1536), "dma_mfma32_f32_64x64x16_w4_s3", 2, 1),
+              ((2048, 2049, 2048), "dma_mfma32_f32_128x128x16_w8_s3", 1, 0),
+              ((3000, 3001, 3000), "dma_mfma32_f32_128x128x16_w8_s3", 4, 1)]
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+@pytest.mark.parametrize("shape,kernel,split,tail", SHORT_STEP,
+                         ids=[f"{m}x{k}x{n}" for (m, k, n), _, _, _ in SHORT_STEP])
+def test_general_short_last_step(ta, tb, shape, kernel, split, tail):
+    M, K, N = shape
+    p = binding.gemm_f32_plan(M, N, K)
+    assert (binding.gemm_kernel_name(p.kernel), p.split_k, p.split_tail) == (kernel, split, tail)
+    say(f"general short last step {'TN'[ta]}{'TN'[tb]} {M}x{K}x{N}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=K + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=K + 1)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=(3, 1, 2))
+    check(got, ref, S, M, N, ldc, f"short last step {ta}{tb} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+@pytest.mark.parametrize("shape,kernel,split,tail", SHORT_STEP[:3],
+                         ids=[f"{m}x{k}x{n}" for (m, k, n), _, _, _ in SHORT_STEP[:3]])
+def test_general_short_last_step_integers_bit_exact(ta, tb, shape, kernel, split, tail):
+    M, K, N = shape
+    say(f"general short last step int {'TN'[ta]}{'TN'[tb]} {M}x{K}x{N}")
+    X, Y = gemm_inputs.draw(M, K, N, "int", seed=K + 3 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "int", seed=7)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 2.0, X, Y, -3.0, C0, pads=(1, 2, 3))
+    check(got, ref, S, M, N, ldc, f"short last step int {ta}{tb} {M}x{K}x{N}", bits=True)
+
+
 @pytest.mark.parametrize("ta,tb,pads", [(0, 0, (0, 0, 0)), (0, 0, (3, 1, 2)), (1, 0, (2, 3, 1)),
                                         (0, 1, (0, 0, 4)), (1, 1, (1, 1, 2))],
                          ids=["NN", "NN-padded", "TN", "NT", "TT"])
