@@ -59,18 +59,18 @@ DEFAULT_TIMED_MS = 20.0
 # (bench.py --copy-probe-mib 256): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
 FETCH_FACTOR = 2.0
 WRITE_FACTOR = 1.0
-_SHA = "2a334f254733453c131c78c6a7765a414fea65c8d13bf1d6ab8e4bd5f4b13b8a"
+_SHA = "4cc3f37300539d1690f8e3e48551f6e2c3c6c6c70cd46a0ddc13472fa8da20d8"
 MEASURED_TRAFFIC = {
     ("square_4096", "dma_mfma32_f32_256x256x16_w8_s3"): {
-        "fetch_kib": 196732.1875, "write_kib": 65536.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 196745.84375, "write_kib": 65536.0, "kernel_source_sha256": _SHA},
     ("longk_512x131072x512", "dma_mfma32_f32_128x128x16_w8_s3"): {
-        "fetch_kib": 262253.0, "write_kib": 16384.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 262262.96875, "write_kib": 16384.0, "kernel_source_sha256": _SHA},
     ("regular_1024x512x1024", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 6239.5, "write_kib": 4096.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 6237.5, "write_kib": 4096.0, "kernel_source_sha256": _SHA},
     ("irregular_1001x513x777", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 6303.375, "write_kib": 3147.59375, "kernel_source_sha256": _SHA},
+        "fetch_kib": 6301.375, "write_kib": 3147.59375, "kernel_source_sha256": _SHA},
     ("small_128x96x112", "dma_mfma32_f32_64x64x16_w4_s3"): {
-        "fetch_kib": 149.5, "write_kib": 56.0, "kernel_source_sha256": _SHA},
+        "fetch_kib": 146.0, "write_kib": 56.0, "kernel_source_sha256": _SHA},
 }
 KERNEL_SOURCE = os.path.join(ROOT, "fp32_gemm_07_amd", "csrc", "gemm_kernels.hpp")
 
@@ -235,13 +235,14 @@ SWEEP_SHAPES = [
     "8192x8192x8192",
 ]
 SWEEP_KERNELS = ["dma32_256x256_w8_s3", "dma32_256x256_w8", "dma32_128x128_w4",
-                 "dma32_128x128_w8_s3", "dma32_128x128_w8", "dma16_128x128_w4", "dma32_64x64_s3",
-                 "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64", "mfma32_128x128",
-                 "mfma32_64x64", "valu_64x64"]
+                 "dma32_128x128_w8_s3", "dma32_128x128_w8", "dma16_128x128_w4", "dma16_96x96_s3",
+                 "dma32_64x64_s3", "dma32_64x64", "dma16_64x64", "dma16_128x64", "mfma16_64x64",
+                 "mfma32_128x128", "mfma32_64x64", "valu_64x64"]
 SWEEP_SPLITS = (1, 2, 4, 8, 16, 32, 64)
 SWEEP_MAX_WORKSPACE = 2 << 30
 # copy-fed kernels that take a split tail, by tile edge
-TAIL_KERNELS = {"dma32_256x256_w8_s3": 256, "dma32_128x128_w8_s3": 128, "dma32_64x64_s3": 64}
+TAIL_KERNELS = {"dma32_256x256_w8_s3": 256, "dma32_128x128_w8_s3": 128, "dma16_96x96_s3": 96,
+                "dma32_64x64_s3": 64}
 
 LADDER_SHAPES = ["1024x512x1024", "1001x513x777"]
 # The walkthrough's rungs v0..v4, then the matrix-core kernels.

@@ -50,6 +50,7 @@ GEMM_KERNEL_DMA16_128x64 = 38
 GEMM_KERNEL_DMA32_128x128_W8 = 39
 GEMM_KERNEL_DMA32_64x64_S3 = 45
 GEMM_KERNEL_DMA32_128x128_W8_S3 = 46
+GEMM_KERNEL_DMA16_96x96_S3 = 47
 GEMM_KERNEL_LADDER_V0 = 40
 GEMM_KERNEL_LADDER_V1 = 41
 GEMM_KERNEL_LADDER_V2 = 42
@@ -78,6 +79,7 @@ KERNELS = {
     "dma32_128x128_w8": GEMM_KERNEL_DMA32_128x128_W8,
     "dma32_64x64_s3": GEMM_KERNEL_DMA32_64x64_S3,
     "dma32_128x128_w8_s3": GEMM_KERNEL_DMA32_128x128_W8_S3,
+    "dma16_96x96_s3": GEMM_KERNEL_DMA16_96x96_S3,
     "valu_64x64": GEMM_KERNEL_VALU_64x64,
     "ladder_v0": GEMM_KERNEL_LADDER_V0,
     "ladder_v1": GEMM_KERNEL_LADDER_V1,

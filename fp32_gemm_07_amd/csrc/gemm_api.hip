@@ -69,6 +69,7 @@ constexpr KernelInfo kKernels[] = {
     {GEMM_KERNEL_DMA32_128x128_W8, 128, 128, 16, "dma_mfma32_f32_128x128x16_w8_s4"},
     {GEMM_KERNEL_DMA32_64x64_S3, 64, 64, 16, "dma_mfma32_f32_64x64x16_w4_s3"},
     {GEMM_KERNEL_DMA32_128x128_W8_S3, 128, 128, 16, "dma_mfma32_f32_128x128x16_w8_s3"},
+    {GEMM_KERNEL_DMA16_96x96_S3, 96, 96, 32, "dma_mfma16_f32_96x96x32_w4_s3"},
     {GEMM_KERNEL_LADDER_V0, 16, 16, 16, "ladder_v0_naive_rows_along_lanes"},
     {GEMM_KERNEL_LADDER_V1, 16, 16, 16, "ladder_v1_naive_cols_along_lanes"},
     {GEMM_KERNEL_LADDER_V2, 16, 16, 16, "ladder_v2_lds_16x16x16"},
@@ -87,7 +88,8 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // split tail).
 bool is_dma_kernel(int id) {
   return (id >= GEMM_KERNEL_DMA32_256x256_W8 && id <= GEMM_KERNEL_DMA32_128x128_W8) ||
-         id == GEMM_KERNEL_DMA32_64x64_S3 || id == GEMM_KERNEL_DMA32_128x128_W8_S3;
+         id == GEMM_KERNEL_DMA32_64x64_S3 || id == GEMM_KERNEL_DMA32_128x128_W8_S3 ||
+         id == GEMM_KERNEL_DMA16_96x96_S3;
 }
 
 struct Resolved {
@@ -178,7 +180,7 @@ bool dma_tile_usable(const Problem &p, int bm, int bn, int bk) {
          (!p.tb || operand_fits(true, bn, p.ldb, 2 * bk));
 }
 
-// The planner: a cost model over four copy-fed kernels and power-of-two
+// The planner: a cost model over five copy-fed kernels and power-of-two
 // K splits, fitted to timings of those kernels over square, wide, long-K and
 // ragged shapes on one MI355X. A CU works through its share of a launch's
 // workgroups (at most n = ceil(workgroups / CUs) of them), so a launch costs
@@ -200,6 +202,7 @@ struct PlanCandidate {
   double eff_shared;          // eff when the launch puts more than one workgroup on a CU
   double per_wg_shared_us;    // per_wg then (one workgroup's store overlaps another's work)
   bool all_orders;            // built for transposed operands too
+  bool paired_tail;           // split tail: pieces may land two to a CU (see plan_cost_us)
 };
 // With two 64x64 workgroups on a CU each SIMD runs two waves, which hide
 // each other's waits: per-wave timestamps give 1,083 clocks per pair of K
@@ -209,11 +212,22 @@ struct PlanCandidate {
 // the other's copies (8192 x 16 x 8192: 52.7 against 62.1 us for 256x256);
 // from K ~ 128 (4096^2) or ~ 200 (8192^2) on it loses to the others
 // (4096 x 256 x 4096: 77.2 against 73.1 us), which its eff_shared is fitted to.
+// The 96 x 96 kernel (16 x 16 blocks, one wave per SIMD) fills the CUs where
+// 64 x 64 and 128 x 128 tiles leave a partial round: 256 tiles at 1536^2
+// (54.8 against 61.3 us for the best 64 x 64 plan), 1024 at 3072^2. Its
+// constants are fitted to 59 shapes (square, wide, long-K, short-K, small
+// and ragged) timed with all five candidates: the planner's plan is within
+// 2 % of the fastest candidate plan on 55 of them (on 43 without this
+// kernel). Its low eff stands for the dearer prologue of short K ranges
+// (333 x 4444 x 555 split in 8: 31.2 against 25.0 us for 64 x 64 tiles). It
+// comes last, so that it takes only plans more than 1 % cheaper than the
+// others' (ties go to the plan seen first).
 constexpr PlanCandidate kPlanCandidates[] = {
-    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966, 11.9, true},
-    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982, 6.9, true},
-    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935, 1.2, true},
-    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, false},
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966, 11.9, true, false},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982, 6.9, true, false},
+    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935, 1.2, true, true},
+    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, false, true},
+    {GEMM_KERNEL_DMA16_96x96_S3, 0.95, 2.0, 4.0, 2, 0.97, 2.0, false, false},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
@@ -240,12 +254,15 @@ double plan_cost_us(const Problem &pr, const PlanCandidate &c, int split, bool t
   // The pieces of a split tail start as the whole tiles end, on whichever CU
   // frees a slot first. A CU holds two workgroups of a 4-wave kernel: with
   // more pieces than half the CUs some CU can take two of them side by side,
-  // so such a round is costed as two. How much that costs depends on how the
-  // whole tiles end: 256 pieces of 64 x 64 tiles after two whole rounds take
-  // 66 against 62 us for 128 pieces at 1500^3 (the rule's choice), but 61
-  // against 63.5 us at 1536^3, where the rule picks the 128 (three runs each);
-  // without the rule the two swap, with no gain over the shapes measured.
-  if (r.dp_tiles > 0 && c.slots_per_cu > 1 && split_tiles * r.splits > cus / 2)
+  // so such a round is costed as two (paired_tail). How much that costs
+  // depends on how the whole tiles end: 256 pieces of 64 x 64 tiles after two
+  // whole rounds take 66 against 62 us for 128 pieces at 1500^3 (the rule's
+  // choice), but 61 against 63.5 us at 1536^3, where the rule picks the 128
+  // (three runs each); without the rule the two swap, with no gain over the
+  // shapes measured. The 96 x 96 kernel's tails follow the plain rounds
+  // (2304^3: 256 pieces 177.1, 512 pieces 183.7 us; 1792^3: 210 pieces 95.3,
+  // 420 pieces 99.9 us).
+  if (r.dp_tiles > 0 && c.paired_tail && split_tiles * r.splits > cus / 2)
     rounds = std::max(rounds, 2.0);
   double us = rounds * per_wg + c.fixed_us;
   if (r.dp_tiles > 0)
@@ -542,6 +559,8 @@ bool launch_gemm_kernel(const Problem &p, void *workspace, const Resolved &r,
       return launch_dma(p, ws, r, slab, stream) ||
              (plain && launch_mfma<32, 64, 64, 16, 2, 2, 2, 2>(A, B, out, M, N, K, r, slab,
                                                                   stream));
+    case GEMM_KERNEL_DMA16_96x96_S3:   // no register-staged kernel of this tile
+      return launch_dma(p, ws, r, slab, stream);
     case GEMM_KERNEL_VALU_64x64: {
       const bool exact = (M % 64 == 0) && (N % 64 == 0) && (K % 16 == 0);
       const dim3 grid(static_cast<unsigned>(r.tiles_m * r.tiles_n * r.splits));

@@ -64,6 +64,8 @@ bool launch_dma_kernel(int kernel, const DmaLaunch &d, hipStream_t stream) {
       return launch_orders<32, 128, 128, 16, 2, 4, 3, 2, true>(d, stream);
     case GEMM_KERNEL_DMA32_64x64_S3:
       return launch_orders<32, 64, 64, 16, 2, 2, 3, 2, true>(d, stream);
+    case GEMM_KERNEL_DMA16_96x96_S3:
+      return launch_orders<16, 96, 96, 32, 2, 2, 3, 2, false>(d, stream);
   }
   return false;
 }

@@ -641,19 +641,36 @@ __device__ inline int swz_k(int r) {
 // (B: BX = BN) by a K step of BK, stored K-contiguous (KMAJOR) or
 // M/N-contiguous in global memory, with row stride ld. Per wave: its share of
 // the stage's copy instructions and its fragment read offsets.
+//
+// M/N-contiguous operands are stored in LDS as BK rows of BX floats, the
+// 16-column blocks of row k flipped by ((k / KS) % NQ) * MI columns (XOR),
+// so the NQ lane groups of a fragment read, which read NQ rows KS apart, hit
+// NQ different 16-bank windows. That needs BX to be a power of two. A width
+// that is not (BX = 96) is stored as BX / 32 panels of 32 columns instead
+// (PANEL), each BK = 32 rows of 32 floats, 16 x 16 blocks only (NQ = 4 lane
+// groups, KS = 8): row k = 8q + c of a panel sits in row slot
+// 16 (q & 1) + 2c + (q >> 1), its two 16-column halves swapped when q is
+// odd. A read by the four lane groups (rows 8q + c, one 16-column half) then
+// lands in four different 16-float windows modulo 64 floats (the slot's
+// parity and the swap tell them apart) and in two different ones modulo 32
+// within each half-wave, so it is free of bank conflicts with 64 banks and
+// with 32. A copy fills 8 row slots of one panel.
 template <int MI, int BX, int BK, int WX, int NW, bool KMAJOR, int VEC>
 struct DmaOperand {
   static constexpr int NQ = 64 / MI;            // lane groups of an instruction
   static constexpr int KS = BK / NQ;            // k per lane group per K step
   static constexpr int NG = KS / 4;             // fragment groups per K step
   static constexpr int F = WX / MI;             // blocks per wave along x
-  static constexpr int ROW = KMAJOR ? BK : BX;  // floats per LDS row
+  static constexpr bool PANEL = !KMAJOR && (BX & (BX - 1)) != 0;
+  static constexpr int ROW = KMAJOR ? BK : (PANEL ? 32 : BX);   // floats per LDS row
   static constexpr int CH = ROW / 4;            // 16-byte chunks per LDS row
   static constexpr int EP = ROW / VEC;          // lanes per LDS row in one copy
   static constexpr int RP = 64 / EP;            // LDS rows per copy
-  static constexpr int I = (KMAJOR ? BX : BK) / RP;   // copies per stage
+  static constexpr int I = KMAJOR ? BX / RP : (BX / ROW) * (BK / RP);   // copies per stage
   static constexpr int L = I / NW;              // copies per wave
   static constexpr int COPY_BYTES = 256 * VEC;  // LDS bytes one copy fills
+  // LDS floats from fragment row k to row k + 1 (M/N-contiguous operands).
+  static constexpr int K_STRIDE = PANEL ? 64 : BX;
   // M/N-contiguous with 4 blocks per wave: block f takes rows (or columns)
   // x = 4*i + f of the wave's range instead of f*MI + i, so a lane's four
   // values at one k are adjacent and one 16-byte read fetches them.
@@ -662,7 +679,9 @@ struct DmaOperand {
   static_assert(VEC == 4 || VEC == 1, "16- or 4-byte copies");
   static_assert(!KMAJOR || CH == 4 || CH == 8, "K step of 16 or 32");
   static_assert(EP <= 64 && 64 % EP == 0, "whole LDS rows per copy");
-  static_assert(KMAJOR || BX >= NQ * MI, "column flips stay inside a row");
+  static_assert(KMAJOR || PANEL || BX >= NQ * MI, "column flips stay inside a row");
+  static_assert(!PANEL || (MI == 16 && BK == 32 && VEC == 4 && BX % 32 == 0 && !INTERLEAVE),
+                "panels: 16x16 blocks, K step 32, 16-byte copies, whole panels");
   static_assert(I % NW == 0, "copies split evenly over waves");
 
   unsigned voff[L];  // lane's byte offset from the tile's first element at step 0
@@ -684,6 +703,17 @@ struct DmaOperand {
         kk[i] = ke;
         voff[i] = ok[i] ? (static_cast<unsigned>(r) * static_cast<unsigned>(ld) + ke) * 4u
                         : kOutOfRange;
+      } else if constexpr (PANEL) {
+        // Row slot sr of panel n / (BK / RP) holds k row 8 grp + c, grp being
+        // the lane group that reads it.
+        const int sr = r % BK;
+        const int grp = 2 * (sr % 2) + sr / 16;
+        const int k = 8 * grp + (sr / 2) % 8;
+        const int xe = 32 * (n / (BK / RP)) + (pe ^ (16 * (grp & 1)));
+        ok[i] = x0 + xe < X;
+        kk[i] = k;
+        voff[i] = ok[i] ? (static_cast<unsigned>(k) * static_cast<unsigned>(ld) + xe) * 4u
+                        : kOutOfRange;
       } else {
         const int xe = pe ^ (((r / KS) % NQ) * MI);              // logical column
         ok[i] = x0 + xe < X;
@@ -703,9 +733,28 @@ struct DmaOperand {
         rd[j] = x * BK + 4 * (((q * KS + 4 * j) / 4) ^ swz_k<CH>(x));
       } else if constexpr (INTERLEAVE) {
         rd[j] = q * KS * BX + ((wx * WX + 4 * li) ^ (q * MI));
+      } else if constexpr (PANEL) {
+        // block j's 16 columns lie in one panel; row 8q + c is at slot
+        // 16 (q & 1) + (q >> 1) + 2c
+        const int x = wx * WX + j * MI + li;
+        rd[j] = (x / 32) * (32 * BK) + (16 * (q & 1) + (q >> 1)) * 32 + ((x % 32) ^ (16 * (q & 1)));
       } else {
         rd[j] = q * KS * BX + ((wx * WX + j * MI + li) ^ (q * MI));
       }
+    }
+  }
+
+  // Reads per fragment group, and read X of load() alone.
+  static constexpr int NREADS = KMAJOR ? F : (INTERLEAVE ? 4 : 4 * F);
+  __device__ inline void load_part(const float *region, int g, int X, floatx4 (&frag)[F]) const {
+    if constexpr (KMAJOR) {
+      frag[X] = *reinterpret_cast<const floatx4 *>(region + rd[g] + X * MI * BK);
+    } else if constexpr (INTERLEAVE) {
+      const floatx4 v = *reinterpret_cast<const floatx4 *>(region + rd[0] + (4 * g + X) * BX);
+#pragma unroll
+      for (int f = 0; f < F; ++f) frag[f][X] = v[f];
+    } else {
+      frag[X % F][X / F] = region[rd[X % F] + (4 * g + X / F) * K_STRIDE];
     }
   }
 
@@ -737,7 +786,7 @@ struct DmaOperand {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int f = 0; f < F; ++f) frag[f][j] = region[rd[f] + (4 * g + j) * BX];
+        for (int f = 0; f < F; ++f) frag[f][j] = region[rd[f] + (4 * g + j) * K_STRIDE];
     }
   }
 };
@@ -796,6 +845,13 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   using acc_t = typename Op::acc_t;
   constexpr int FM = S::FM, FN = S::FN, NG = S::NG, LPW = S::LPW;
   constexpr int STAGE_F = S::STAGE_BYTES / 4;
+  // A wave with more than 4 copies per step (one wave per SIMD, 16 x 16
+  // blocks: a 32-clock MFMA is all that covers a stall) interleaves the main
+  // loop's fragment reads and copies with its MFMAs one by one (group_spread)
+  // instead of issuing them in bursts: the reads of a CU's waves share the
+  // LDS and their copies one address unit, so a burst keeps a wave from its
+  // next MFMA while it waits for its turn there.
+  constexpr bool kSpreadCopies = LPW > 4;
 
   // The stages, then one float of padding that no copy writes: a real store
   // into it keeps the compiler from treating the array as never written (the
@@ -878,27 +934,42 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // Copies of a step whose K range is whole and not the last: no chunk
   // crosses the end of an operand, so the step's advance goes in soffset and
   // the lane offsets stay loop-invariant (no vector add in front of a copy).
-  auto issue_full = [&](int step, unsigned stage_byte) {
+  // Copies c0 .. c1-1 of the wave's LPW (A's first, then B's).
+  auto issue_full_part = [&](int step, unsigned stage_byte, auto c0_c, auto c1_c) {
+    constexpr int C0 = decltype(c0_c)::value, C1 = decltype(c1_c)::value;
     const unsigned da = a_step * step, db = b_step * step;
 #pragma unroll
     for (int i = 0; i < OpA::L; ++i)
-      dma_copy_soff<VEC>(ra, opa.voff[i], da, stage_byte + opa.lds[i]);
+      if (i >= C0 && i < C1) dma_copy_soff<VEC>(ra, opa.voff[i], da, stage_byte + opa.lds[i]);
 #pragma unroll
     for (int i = 0; i < OpB::L; ++i)
-      dma_copy_soff<VEC>(rb, opb.voff[i], db, stage_byte + S::A_BYTES + opb.lds[i]);
+      if (OpA::L + i >= C0 && OpA::L + i < C1)
+        dma_copy_soff<VEC>(rb, opb.voff[i], db, stage_byte + S::A_BYTES + opb.lds[i]);
   };
-  // Copies of any step: chunks past the end of the K range read zeros.
-  auto issue_checked = [&](int step, unsigned stage_byte) {
+  auto issue_full = [&](int step, unsigned stage_byte) {
+    issue_full_part(step, stage_byte, std::integral_constant<int, 0>(),
+                    std::integral_constant<int, LPW>());
+  };
+  // Copies of any step: chunks past the end of the K range read zeros
+  // (copies c0 .. c1-1 of the wave's LPW, or all).
+  auto issue_checked_part = [&](int step, unsigned stage_byte, auto c0_c, auto c1_c) {
+    constexpr int C0 = decltype(c0_c)::value, C1 = decltype(c1_c)::value;
     const int kr = k_end - (k_begin + step * BK);   // K elements left in this step
     const unsigned da = a_step * step, db = b_step * step;
 #pragma unroll
     for (int i = 0; i < OpA::L; ++i)
-      dma_copy<VEC>(ra, opa.k_valid(i, kr) ? opa.voff[i] + da : kOutOfRange,
-                    stage_byte + opa.lds[i]);
+      if (i >= C0 && i < C1)
+        dma_copy<VEC>(ra, opa.k_valid(i, kr) ? opa.voff[i] + da : kOutOfRange,
+                      stage_byte + opa.lds[i]);
 #pragma unroll
     for (int i = 0; i < OpB::L; ++i)
-      dma_copy<VEC>(rb, opb.k_valid(i, kr) ? opb.voff[i] + db : kOutOfRange,
-                    stage_byte + S::A_BYTES + opb.lds[i]);
+      if (OpA::L + i >= C0 && OpA::L + i < C1)
+        dma_copy<VEC>(rb, opb.k_valid(i, kr) ? opb.voff[i] + db : kOutOfRange,
+                      stage_byte + S::A_BYTES + opb.lds[i]);
+  };
+  auto issue_checked = [&](int step, unsigned stage_byte) {
+    issue_checked_part(step, stage_byte, std::integral_constant<int, 0>(),
+                       std::integral_constant<int, LPW>());
   };
   // Wait until this wave's copies of a step have landed while the copies of
   // `later` steps issued after it may stay in flight (vmcnt counts this
@@ -1027,6 +1098,60 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     }
   };
 
+  // In the last step of the K range only kr_last elements (1 .. BK) are
+  // real; instruction s of a step (4 * group + j) takes k = q*KS + s for lane
+  // group q, so from s = kr_last on it would only add the zero fill: skipped,
+  // and so are fragment reads that only such instructions would use. (A
+  // zero-fill product adds +0.0, which leaves an accumulator's bits as they
+  // are: it starts at +0.0 and never becomes -0.0.)
+  const int kr_last = k_end - (k_begin + (nk - 1) * BK);
+  // Whether any instruction of the last step can be skipped: instruction s
+  // is needed while s < kr_last, and a step has KS of them. Otherwise the
+  // last step runs without the per-instruction branches (they cost ~15
+  // clocks each in front of an MFMA).
+  const bool skip_some = kr_last < S::KS;
+
+  // One fragment group g of the spread schedule: its 4 * FM * FN MFMAs (by
+  // instruction, then block) from fragment slot `slot` (in the final step of
+  // the range only the instructions it needs), the reads of the next
+  // group's fragments (group rd_g of region rd_st, into slot ^ 1; if
+  // `reads`) two after each of the first MFMAs, then (copy mode CM: 1 whole
+  // step, 2 range-checked) the LPW copies of step cp_step into stage byte
+  // cp_stage one after every third MFMA from the group's second quarter on.
+  constexpr int kNm = 4 * FM * FN;
+  constexpr int kNra = OpA::NREADS, kNr = kNra + OpB::NREADS;
+  auto group_spread = [&](int slot, int g, bool final_step, bool reads, const float *rd_st,
+                          int rd_g, auto cm_c, int cp_step, unsigned cp_stage) {
+    constexpr int CM = decltype(cm_c)::value;
+    constexpr int NC = CM ? LPW : 0;
+    static_assert(kNr <= 2 * (kNm / 4) && kNm / 4 + 3 * LPW <= kNm, "side work fits the group");
+    unroll_steps<0, kNm>([&](auto m_c) {
+      constexpr int Mi = decltype(m_c)::value;
+      constexpr int j = Mi / (FM * FN), fm = (Mi % (FM * FN)) / FN, fn = Mi % FN;
+      if (!final_step || !skip_some || 4 * g + j < kr_last)
+        acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (reads) {
+        unroll_steps<2 * Mi, 2 * Mi + 2>([&](auto x_c) {
+          constexpr int X = decltype(x_c)::value;
+          if constexpr (X < kNra) opa.load_part(rd_st, rd_g, X, fa[slot ^ 1]);
+          else if constexpr (X < kNr)
+            opb.load_part(rd_st + S::A_BYTES / 4, rd_g, X - kNra, fb[slot ^ 1]);
+        });
+      }
+      constexpr int C = (Mi - kNm / 4) / 3;
+      if constexpr (Mi >= kNm / 4 && (Mi - kNm / 4) % 3 == 0 && C < NC) {
+        if constexpr (CM == 1)
+          issue_full_part(cp_step, cp_stage, std::integral_constant<int, C>(),
+                          std::integral_constant<int, C + 1>());
+        else
+          issue_checked_part(cp_step, cp_stage, std::integral_constant<int, C>(),
+                             std::integral_constant<int, C + 1>());
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
   // Schedule. One barrier per K step t, in its last fragment group. Every
   // read of step t's stage was issued before it (the fragments of a step are
   // read during the step before it and the step itself), so right after it
@@ -1063,6 +1188,22 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     constexpr int ST = decltype(stage_c)::value;
     const float *st = smem + ST * STAGE_F;
     const float *st_next = smem + ((ST + 1) % NS) * STAGE_F;
+    if constexpr (kSpreadCopies) {
+      unroll_steps<0, NG>([&](auto g_c) {
+        constexpr int G = decltype(g_c)::value;
+        constexpr int slot = (ST * NG + G) & 1;
+        if constexpr (G < NG - 1) {
+          group_spread(slot, G, false, true, st, G + 1, std::integral_constant<int, 0>(), 0, 0u);
+        } else {
+          wait_vmcnt<(NS - 2) * LPW>();
+          barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          group_spread(slot, G, false, true, st_next, 0, std::integral_constant<int, 1>(), t + NS,
+                       smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
+        }
+      });
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int slot = (ST * NG + g) & 1;
@@ -1089,18 +1230,6 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
       }
     }
   };
-  // In the last step of the K range only kr_last elements (1 .. BK) are
-  // real; instruction s of a step (4 * group + j) takes k = q*KS + s for lane
-  // group q, so from s = kr_last on it would only add the zero fill: skipped,
-  // and so are fragment reads that only such instructions would use. (A
-  // zero-fill product adds +0.0, which leaves an accumulator's bits as they
-  // are: it starts at +0.0 and never becomes -0.0.)
-  const int kr_last = k_end - (k_begin + (nk - 1) * BK);
-  // Whether any instruction of the last step can be skipped: instruction s
-  // is needed while s < kr_last, and a step has KS of them. Otherwise the
-  // last step runs without the per-instruction branches (they cost ~15
-  // clocks each in front of an MFMA).
-  const bool skip_some = kr_last < S::KS;
   auto mfma_k = [&](int slot, int g, int j, bool final_step) {
     if (!final_step || !skip_some || 4 * g + j < kr_last) mfma_step(slot, j);
   };
@@ -1118,6 +1247,28 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     // Steps up to min(R-1, J+NS-1) have been issued; step J+1 must land.
     constexpr int kLater = (R - 1 < J + NS - 1 ? R - 1 : J + NS - 1) - (J + 1);
     const float *st = smem + ST * STAGE_F;
+    if constexpr (kSpreadCopies) {
+      unroll_steps<0, NG>([&](auto g_c) {
+        constexpr int G = decltype(g_c)::value;
+        constexpr int slot = ((J & 1) * NG + G) & 1;
+        if constexpr (G < NG - 1) {
+          group_spread(slot, G, !kMore, kMore || 4 * (G + 1) < kr_last, st, G + 1,
+                       std::integral_constant<int, 0>(), 0, 0u);
+        } else {
+          if constexpr (kMore) {
+            wait_vmcnt<kLater * LPW>();
+            if constexpr (J + 2 == R) zero_k_tail(t0 + J + 1);
+            barrier();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          constexpr int kMode = !kIssue ? 0 : (J + NS < R - 1 ? 1 : 2);
+          group_spread(slot, G, !kMore, kMore, smem + ((ST + 1) % NS) * STAGE_F, 0,
+                       std::integral_constant<int, kMode>(), t0 + J + NS,
+                       smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
+        }
+      });
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int slot = ((J & 1) * NG + g) & 1;

@@ -142,15 +142,22 @@ def test_planner_choices_for_standing_workloads():
 
 
 def test_split_tail_plans():
-    """Split tail: the planner's plan where 576 tiles of 64 x 64 leave a last
-    round of 64 (split in two: 128 pieces, at most one per CU; four-way, 256
-    pieces, would put two on some CU); workspace sizes for whole rounds, a
-    partial round and fewer tiles than one round; plans the library must
-    reject."""
-    p = binding.gemm_f32_plan(1536, 1536, 1536)
+    """Split tail: the planner's plans where 18 x 16 tiles of 64 x 64 leave a
+    last round of 32 (1100 x 777 x 1000, split in two) and where 19 x 19 tiles
+    of 96 x 96 leave one of 105 (1792^3, split in two: 210 pieces); none where
+    16 x 16 tiles of 96 x 96 make exactly one round (1536^3); workspace sizes
+    for whole rounds, a partial round and fewer tiles than one round; plans
+    the library must reject."""
+    p = binding.gemm_f32_plan(1100, 1000, 777)
     assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3
-    assert p.split_tail == 1 and p.split_k == 2 and p.k_chunk == 768
-    assert binding.gemm_f32_workspace_bytes(1536, 1536, 1536) == 4 * 2 * 1536 * 1536
+    assert p.split_tail == 1 and p.split_k == 2 and p.k_chunk == 400
+    assert binding.gemm_f32_workspace_bytes(1100, 1000, 777) == 4 * 2 * 1100 * 1000
+    p = binding.gemm_f32_plan(1792, 1792, 1792)
+    assert p.kernel == binding.GEMM_KERNEL_DMA16_96x96_S3
+    assert p.split_tail == 1 and p.split_k == 2 and p.k_chunk == 896
+    p = binding.gemm_f32_plan(1536, 1536, 1536)
+    assert p.kernel == binding.GEMM_KERNEL_DMA16_96x96_S3 and p.split_k == 1
+    assert binding.gemm_f32_workspace_bytes(1536, 1536, 1536) == 0
     tail = binding.make_plan(binding.GEMM_KERNEL_DMA32_64x64_S3, 4, True)
     # 16 x 16 = 256 tiles: one whole round, nothing split
     assert binding.gemm_f32_plan_workspace_bytes(1024, 1024, 1024, tail) == 0
@@ -260,10 +267,17 @@ def test_plans_follow_the_compute_unit_count():
         a, b = binding.gemm_f32_plan(M, N, K), binding.gemm_f32_plan_cus(M, N, K, 256)
         assert (a.kernel, a.split_k, a.k_chunk, a.split_tail) == \
             (b.kernel, b.split_k, b.k_chunk, b.split_tail)
-    # 576 tiles of 64 x 64: 2 rounds + 64 tiles at 256 CUs (split tail),
-    # exactly 3 rounds at 192 (nothing split)
-    p = binding.gemm_f32_plan_cus(1536, 1536, 1536, 256)
+    # 288 tiles of 64 x 64: a round + 32 tiles at 256 CUs (split tail),
+    # exactly one round at 288 (nothing split)
+    p = binding.gemm_f32_plan_cus(1100, 1000, 777, 256)
     assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_tail == 1 and p.split_k == 2
+    p = binding.gemm_f32_plan_cus(1100, 1000, 777, 288)
+    assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_tail == 0 and p.split_k == 1
+    # 1536^3: 256 tiles of 96 x 96, one round at 256 CUs; at 192 a third of
+    # them would make a second round, while 576 tiles of 64 x 64 make exactly
+    # three
+    p = binding.gemm_f32_plan_cus(1536, 1536, 1536, 256)
+    assert p.kernel == binding.GEMM_KERNEL_DMA16_96x96_S3 and p.split_k == 1
     p = binding.gemm_f32_plan_cus(1536, 1536, 1536, 192)
     assert p.kernel == binding.GEMM_KERNEL_DMA32_64x64_S3 and p.split_tail == 0 and p.split_k == 1
     # 256 tiles of 256 x 256: one round at 256 CUs, two whole rounds at 128

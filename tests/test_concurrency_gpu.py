@@ -15,7 +15,7 @@ from gpu_util import nan_buffer, say, to_dev, torch
 pytestmark = pytest.mark.gpu
 
 # (M, K, N): unsplit, split K (every tile), split tail, ragged
-SHAPES = [(1001, 513, 777), (256, 8192, 256), (1536, 1536, 1536), (300, 2000, 260)]
+SHAPES = [(1001, 513, 777), (256, 8192, 256), (1792, 1792, 1792), (300, 2000, 260)]
 
 
 def _case(M, K, N, seed):
@@ -146,7 +146,7 @@ def test_library_workspace_overlapping_streams():
     results bit-identical to each call made alone."""
     t = torch()
     say("library workspace: overlapping split-K calls on two streams")
-    shapes = [(256, 16384, 256), (1536, 1536, 1536), (512, 8192, 384)]
+    shapes = [(256, 16384, 256), (1792, 1792, 1792), (512, 8192, 384)]
     assert all(binding.gemm_f32_plan(M, N, K).split_k > 1 for M, K, N in shapes)
     cases = [_lib_case(M, K, N, seed=30 + i) for i, (M, K, N) in enumerate(shapes)]
     expected = [_lib_alone(c) for c in cases]
@@ -175,7 +175,7 @@ def test_library_workspace_grows_while_a_buffer_is_in_use():
     small = _lib_case(128, 8192, 128, seed=40)
     bigger = [_lib_case(M, K, N, seed=41 + i)
               for i, (M, K, N) in enumerate([(256, 16384, 256), (512, 32768, 512),
-                                             (640, 16384, 640), (768, 16384, 768)])]
+                                             (640, 16384, 640), (800, 32768, 800)])]
     needs = [binding.gemm_f32_workspace_bytes(c["M"], c["N"], c["K"]) for c in [small] + bigger]
     assert all(a < b for a, b in zip(needs, needs[1:])), needs
     exp_small = _lib_alone(small)

@@ -232,20 +232,42 @@ def test_general_large_tile_ragged(ta, tb):
     check(got, ref, S, M, N, ldc, "256-tile ragged general")
 
 
-@pytest.mark.parametrize("ta,tb,pads", [(0, 0, (0, 0, 0)), (1, 0, (2, 3, 1)), (0, 1, (0, 0, 4)),
-                                        (1, 1, (1, 1, 2))], ids=["NN", "TN", "NT", "TT"])
-def test_general_split_tail(ta, tb, pads):
-    """1536^3, whose plan splits only the last round of tiles: the reduction
-    of the split tiles applies alpha, beta and ldc (row strides that are and
-    are not multiples of 4), the whole tiles are stored directly; every output
+GENERAL_TAILS = [((1100, 777, 1000), 0, 0, (0, 0, 0)), ((1100, 777, 1000), 1, 0, (2, 3, 1)),
+                 ((1100, 777, 1000), 0, 1, (0, 0, 4)), ((1100, 777, 1000), 1, 1, (1, 1, 2)),
+                 ((1792, 1792, 1792), 0, 0, (0, 0, 0)), ((1792, 1792, 1792), 0, 0, (3, 1, 2))]
+
+
+@pytest.mark.parametrize("shape,ta,tb,pads", GENERAL_TAILS,
+                         ids=[f"{m}x{k}x{n}-{'TN'[a]}{'TN'[b]}-{''.join(map(str, p))}"
+                              for (m, k, n), a, b, p in GENERAL_TAILS])
+def test_general_split_tail(shape, ta, tb, pads):
+    """Shapes whose plans split only the last round of tiles (64 x 64 tiles in
+    every storage order, 96 x 96 for untransposed operands): the reduction of
+    the split tiles applies alpha, beta and ldc (row strides that are and are
+    not multiples of 4), the whole tiles are stored directly; every output
     against the oracle."""
-    M = N = K = 1536
+    M, K, N = shape
     assert binding.gemm_f32_plan(M, N, K).split_tail == 1
-    say(f"general split tail {'TN'[ta]}{'TN'[tb]} pads {pads}")
+    say(f"general split tail {M}x{K}x{N} {'TN'[ta]}{'TN'[tb]} pads {pads}")
     X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=100 + ta + 2 * tb)
     C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=101)[0]
     got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
     check(got, ref, S, M, N, ldc, "split tail general")
+
+
+@pytest.mark.parametrize("pads", [(0, 0, 0), (3, 1, 2)], ids=["dense", "padded"])
+def test_general_96_tiles(pads):
+    """1536^3: 16 x 16 tiles of 96 x 96, one per CU, none split (untransposed
+    operands): alpha, beta and row strides through the 96 x 96 kernel's own
+    stores; every output against the oracle."""
+    M = N = K = 1536
+    p = binding.gemm_f32_plan(M, N, K)
+    assert binding.gemm_kernel_name(p.kernel) == "dma_mfma16_f32_96x96x32_w4_s3" and p.split_k == 1
+    say(f"general 96 x 96 tiles pads {pads}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=111)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=112)[0]
+    got, ref, S, ldc = run_general(0, 0, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
+    check(got, ref, S, M, N, ldc, "96 x 96 general")
 
 
 # A last K step of 1 to 4 elements in the planner's plans: the kernels with few
@@ -255,9 +277,9 @@ def test_general_split_tail(ta, tb, pads):
 # range of the split ones), the 8-wave 128 x 128 kernel whole and with a split
 # tail; every storage order, alpha, beta and padded rows.
 SHORT_STEP = [((256, 8193, 256), "dma_mfma32_f32_64x64x16_w4_s3", 16, 0),
-              ((1536, 1540, 1536), "dma_mfma32_f32_64x64x16_w4_s3", 2, 1),
+              ((1100, 785, 1000), "dma_mfma32_f32_64x64x16_w4_s3", 2, 1),
               ((2048, 2049, 2048), "dma_mfma32_f32_128x128x16_w8_s3", 1, 0),
-              ((3000, 3001, 3000), "dma_mfma32_f32_128x128x16_w8_s3", 4, 1)]
+              ((3200, 3201, 3200), "dma_mfma32_f32_128x128x16_w8_s3", 2, 1)]
 
 
 @pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
@@ -377,7 +399,7 @@ def test_general_long_k_full_size_every_element(ta, tb):
 # oracle's reading, within the tolerance of either).
 
 EPILOGUE_CASES = [(64, 1, 64, "direct store"), (128, 16384, 128, "split-K reduction"),
-                  (1536, 1536, 1536, "split tail: direct store and tail reduction")]
+                  (1792, 1792, 1792, "split tail: direct store and tail reduction")]
 
 
 def epilogue_operands(M, K, N, seed):
@@ -404,7 +426,7 @@ def test_general_epilogue_rounds_beta_c_then_fuses(M, K, N, path):
     plan = binding.gemm_f32_plan(M, N, K)
     say(f"epilogue rounding {M}x{K}x{N} ({path}) plan {plan}")
     if K > 1:
-        assert plan.split_k > 1 and plan.split_tail == (1 if M == 1536 else 0)
+        assert plan.split_k > 1 and plan.split_tail == (1 if M == 1792 else 0)
     alpha, beta, X, Y, C0, fused, single = epilogue_operands(M, K, N, seed=M + K)
     differ = fused.view(np.uint32) != single.view(np.uint32)
     assert differ.mean() > 0.01, "operands do not tell the two roundings apart"

@@ -174,7 +174,7 @@ def test_split_tail_integers_bit_exact(kname, t, M, K, N):
 # every copy-fed kernel, whole K and split in two.
 
 DMA_KERNELS = [k for k in binding.KERNELS if k.startswith("dma")]
-K_STEP = {k: (32 if k in ("dma16_64x64", "dma16_128x64") else 16) for k in DMA_KERNELS}
+K_STEP = {k: (32 if k.startswith("dma16_") and k != "dma16_128x128_w4" else 16) for k in DMA_KERNELS}
 STEP_COUNTS = [(n, -5) for n in range(1, 17)] + [(n, 0) for n in (6, 7, 8, 10, 11, 15)]
 
 
@@ -227,18 +227,25 @@ def test_short_last_step_integers_bit_exact(kname, r, split):
     assert_bits_equal(C, C_ref, f"{kname} int K {K} split {split}")
 
 
-def test_split_tail_planner_1536():
-    """1536^3: the planner splits the last round of 64 tiles of 64 x 64 two
-    ways; every output against the oracle, a rerun bit-identical, caller and
+PLANNER_TAILS = [((1100, 777, 1000), "dma_mfma32_f32_64x64x16_w4_s3"),
+                 ((1792, 1792, 1792), "dma_mfma16_f32_96x96x32_w4_s3")]
+
+
+@pytest.mark.parametrize("shape,kernel", PLANNER_TAILS, ids=[k for _, k in PLANNER_TAILS])
+def test_split_tail_planner(shape, kernel):
+    """The planner's split tails: 18 x 16 tiles of 64 x 64 (the last round of
+    32 split two ways) and 19 x 19 tiles of 96 x 96 (the last 105 split two
+    ways); every output against the oracle, a rerun bit-identical, caller and
     library workspaces bit-identical."""
-    M = N = K = 1536
+    M, K, N = shape
     plan = binding.gemm_f32_plan(M, N, K)
-    say(f"split tail planner 1536^3 plan {plan}")
+    say(f"split tail planner {M}x{K}x{N} plan {plan}")
+    assert binding.gemm_kernel_name(plan.kernel) == kernel
     assert plan.split_tail == 1 and plan.split_k > 1
     A, B = gemm_inputs.draw(M, K, N, "uniform", seed=15)
     C1 = run(A, B)
     C_ref, S = oracle.gemm(A, B)
-    assert_within_bound(C1, C_ref, S, "1536^3 split tail")
+    assert_within_bound(C1, C_ref, S, f"{M}x{K}x{N} split tail")
     assert_bits_equal(run(A, B), C1, "rerun")
     assert_bits_equal(run(A, B, entry="gemm_f32_ex"), C1, "caller workspace")
 

@@ -18,8 +18,8 @@ from gpu_util import say, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
-# 1536^3: the plan splits only the last round of tiles (its own reduction).
-CASES = [(1001, 513, 777, "plain"), (256, 8192, 256, "plain"), (1536, 1536, 1536, "plain"),
+# 1792^3: the plan splits only the last round of tiles (its own reduction).
+CASES = [(1001, 513, 777, "plain"), (256, 8192, 256, "plain"), (1792, 1792, 1792, "plain"),
          (300, 513, 260, "general")]
 
 

@@ -33,7 +33,7 @@ def _both(A, B):
 
 # (M, K, N): the long-K workload (K split 16 ways: 16 MiB of partial sums),
 # then smaller split plans, a split-tail plan and an unsplit one.
-CALLS = [(512, 131072, 512), (256, 16384, 256), (1536, 1536, 1536), (100, 3000, 70),
+CALLS = [(512, 131072, 512), (256, 16384, 256), (1792, 1792, 1792), (100, 3000, 70),
          (1001, 513, 777)]
 
 
