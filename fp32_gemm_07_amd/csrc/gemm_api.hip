@@ -203,6 +203,7 @@ struct PlanCandidate {
   double per_wg_shared_us;    // per_wg then (one workgroup's store overlaps another's work)
   bool all_orders;            // built for transposed operands too
   bool paired_tail;           // split tail: pieces may land two to a CU (see plan_cost_us)
+  int min_k;                  // not considered for shorter K
 };
 // With two 64x64 workgroups on a CU each SIMD runs two waves, which hide
 // each other's waits: per-wave timestamps give 1,083 clocks per pair of K
@@ -221,13 +222,16 @@ struct PlanCandidate {
 // kernel). Its low eff stands for the dearer prologue of short K ranges
 // (333 x 4444 x 555 split in 8: 31.2 against 25.0 us for 64 x 64 tiles). It
 // comes last, so that it takes only plans more than 1 % cheaper than the
-// others' (ties go to the plan seen first).
+// others' (ties go to the plan seen first), and only from K = 64 (two of its
+// K steps): below that the fill of its three 24 KiB stages is most of a
+// launch that the model's other candidates are costed too dearly for
+// (2048 x 16 x 2048: 10.1 us against 9.0 for 128 x 128 tiles).
 constexpr PlanCandidate kPlanCandidates[] = {
-    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966, 11.9, true, false},
-    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982, 6.9, true, false},
-    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935, 1.2, true, true},
-    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, false, true},
-    {GEMM_KERNEL_DMA16_96x96_S3, 0.95, 2.0, 4.0, 2, 0.97, 2.0, false, false},
+    {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966, 11.9, true, false, 0},
+    {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982, 6.9, true, false, 0},
+    {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935, 1.2, true, true, 0},
+    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, false, true, 0},
+    {GEMM_KERNEL_DMA16_96x96_S3, 0.95, 2.0, 4.0, 2, 0.97, 2.0, false, false, 64},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU
 constexpr double kReduceBytesPerUs = 8.0e6;           // split-K partial sums
@@ -293,6 +297,7 @@ PlanChoice plan(int M, int N, int K, int cus, const Problem *general = nullptr) 
   Problem pr = general ? *general : plain_problem(nullptr, nullptr, nullptr, M, N, K);
   pr.K = K;
   for (const PlanCandidate &c : kPlanCandidates) {
+    if (K < c.min_k) continue;
     if (general) {
       const KernelInfo *k = find_kernel(c.kernel);
       if (!c.all_orders && (general->ta || general->tb)) continue;

@@ -135,6 +135,13 @@ def test_planner_choices_for_standing_workloads():
         assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_128x128_W4
     for (M, N, K) in [(4096, 4096, 256), (8192, 8192, 256), (4001, 3999, 301)]:
         assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_256x256_W8_S3
+    # 96 x 96 tiles where they fill the CUs (1536^2: one round), from K = 64
+    # on; below that the fill of their stages costs more than it saves
+    # (2048 x 16 x 2048: 10.1 against 9.0 us for 128 x 128 tiles)
+    for K in (64, 128, 1536):
+        assert binding.gemm_f32_plan(1536, 1536, K).kernel == binding.GEMM_KERNEL_DMA16_96x96_S3
+    for (M, N, K) in [(2048, 2048, 16), (1024, 1024, 16), (1536, 1536, 32)]:
+        assert binding.gemm_f32_plan(M, N, K).kernel != binding.GEMM_KERNEL_DMA16_96x96_S3
     for (M, N, K) in [(128, 112, 96), (1024, 1024, 512), (1001, 777, 513), (1, 1, 1)]:
         p = binding.gemm_f32_plan(M, N, K)
         assert p.split_k >= 1 and p.k_chunk * p.split_k >= K

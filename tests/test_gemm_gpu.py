@@ -480,7 +480,7 @@ def test_operand_past_2gib_offsets():
 # add a NaN nor hide one.
 
 SPECIAL_KERNELS = ["dma32_256x256_w8_s3", "dma32_128x128_w8_s3", "dma32_64x64_s3",
-                   "dma32_128x128_w4"]
+                   "dma32_128x128_w4", "dma16_96x96_s3"]
 
 
 def _check_special_values(kname, plan, M, K, N, i0, k0, k1, j1, zeros):
