@@ -1111,34 +1111,32 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // clocks each in front of an MFMA).
   const bool skip_some = kr_last < S::KS;
 
-  // One fragment group g of the spread schedule: its 4 * FM * FN MFMAs (by
-  // instruction, then block) from fragment slot `slot` (in the final step of
-  // the range only the instructions it needs), the reads of the next
-  // group's fragments (group rd_g of region rd_st, into slot ^ 1; if
-  // `reads`) two after each of the first MFMAs, then (copy mode CM: 1 whole
-  // step, 2 range-checked) the LPW copies of step cp_step into stage byte
-  // cp_stage one after every third MFMA from the group's second quarter on.
+  // One fragment group of the spread schedule (steps before the range's
+  // last): its 4 * FM * FN MFMAs (by instruction, then block) from fragment
+  // slot `slot`, the reads of the next group's fragments (group rd_g of
+  // region rd_st, into slot ^ 1) two after each of the first MFMAs, then
+  // (copy mode CM: 1 whole step, 2 range-checked) the LPW copies of step
+  // cp_step into stage byte cp_stage one after every third MFMA from the
+  // group's second quarter on.
   constexpr int kNm = 4 * FM * FN;
   constexpr int kNra = OpA::NREADS, kNr = kNra + OpB::NREADS;
-  auto group_spread = [&](int slot, int g, bool final_step, bool reads, const float *rd_st,
-                          int rd_g, auto cm_c, int cp_step, unsigned cp_stage) {
+  auto group_spread = [&](int slot, const float *rd_st, int rd_g, auto cm_c, int cp_step,
+                          unsigned cp_stage) {
     constexpr int CM = decltype(cm_c)::value;
     constexpr int NC = CM ? LPW : 0;
-    static_assert(kNr <= 2 * (kNm / 4) && kNm / 4 + 3 * LPW <= kNm, "side work fits the group");
+    static_assert(!kSpreadCopies || (kNr <= 2 * (kNm / 4) && kNm / 4 + 3 * LPW <= kNm),
+                  "side work fits the group");
     unroll_steps<0, kNm>([&](auto m_c) {
       constexpr int Mi = decltype(m_c)::value;
       constexpr int j = Mi / (FM * FN), fm = (Mi % (FM * FN)) / FN, fn = Mi % FN;
-      if (!final_step || !skip_some || 4 * g + j < kr_last)
-        acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
+      acc[fm][fn] = Op::run(fa[slot][fm][j], fb[slot][fn][j], acc[fm][fn]);
       __builtin_amdgcn_sched_barrier(0);
-      if (reads) {
-        unroll_steps<2 * Mi, 2 * Mi + 2>([&](auto x_c) {
-          constexpr int X = decltype(x_c)::value;
-          if constexpr (X < kNra) opa.load_part(rd_st, rd_g, X, fa[slot ^ 1]);
-          else if constexpr (X < kNr)
-            opb.load_part(rd_st + S::A_BYTES / 4, rd_g, X - kNra, fb[slot ^ 1]);
-        });
-      }
+      unroll_steps<2 * Mi, 2 * Mi + 2>([&](auto x_c) {
+        constexpr int X = decltype(x_c)::value;
+        if constexpr (X < kNra) opa.load_part(rd_st, rd_g, X, fa[slot ^ 1]);
+        else if constexpr (X < kNr)
+          opb.load_part(rd_st + S::A_BYTES / 4, rd_g, X - kNra, fb[slot ^ 1]);
+      });
       constexpr int C = (Mi - kNm / 4) / 3;
       if constexpr (Mi >= kNm / 4 && (Mi - kNm / 4) % 3 == 0 && C < NC) {
         if constexpr (CM == 1)
@@ -1193,12 +1191,12 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
         constexpr int G = decltype(g_c)::value;
         constexpr int slot = (ST * NG + G) & 1;
         if constexpr (G < NG - 1) {
-          group_spread(slot, G, false, true, st, G + 1, std::integral_constant<int, 0>(), 0, 0u);
+          group_spread(slot, st, G + 1, std::integral_constant<int, 0>(), 0, 0u);
         } else {
           wait_vmcnt<(NS - 2) * LPW>();
           barrier();
           __builtin_amdgcn_sched_barrier(0);
-          group_spread(slot, G, false, true, st_next, 0, std::integral_constant<int, 1>(), t + NS,
+          group_spread(slot, st_next, 0, std::integral_constant<int, 1>(), t + NS,
                        smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
         }
       });
@@ -1247,22 +1245,22 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
     // Steps up to min(R-1, J+NS-1) have been issued; step J+1 must land.
     constexpr int kLater = (R - 1 < J + NS - 1 ? R - 1 : J + NS - 1) - (J + 1);
     const float *st = smem + ST * STAGE_F;
-    if constexpr (kSpreadCopies) {
+    // The final step issues no copies and reads at most its own next group:
+    // it takes the plain form below, whose instruction skip branches once per
+    // instruction index rather than once per MFMA.
+    if constexpr (kSpreadCopies && kMore) {
       unroll_steps<0, NG>([&](auto g_c) {
         constexpr int G = decltype(g_c)::value;
         constexpr int slot = ((J & 1) * NG + G) & 1;
         if constexpr (G < NG - 1) {
-          group_spread(slot, G, !kMore, kMore || 4 * (G + 1) < kr_last, st, G + 1,
-                       std::integral_constant<int, 0>(), 0, 0u);
+          group_spread(slot, st, G + 1, std::integral_constant<int, 0>(), 0, 0u);
         } else {
-          if constexpr (kMore) {
-            wait_vmcnt<kLater * LPW>();
-            if constexpr (J + 2 == R) zero_k_tail(t0 + J + 1);
-            barrier();
-          }
+          wait_vmcnt<kLater * LPW>();
+          if constexpr (J + 2 == R) zero_k_tail(t0 + J + 1);
+          barrier();
           __builtin_amdgcn_sched_barrier(0);
           constexpr int kMode = !kIssue ? 0 : (J + NS < R - 1 ? 1 : 2);
-          group_spread(slot, G, !kMore, kMore, smem + ((ST + 1) % NS) * STAGE_F, 0,
+          group_spread(slot, smem + ((ST + 1) % NS) * STAGE_F, 0,
                        std::integral_constant<int, kMode>(), t0 + J + NS,
                        smem_base + static_cast<unsigned>(ST * S::STAGE_BYTES));
         }
