@@ -18,8 +18,8 @@ void launch_t(const DmaLaunch &d, hipStream_t stream) {
 }
 
 // ALL_ORDERS: the configuration is built for transposed operands too (the
-// planner's 256x256, 8-wave 128x128 and 64x64 kernels); the others take
-// op(A) = A, op(B) = B only.
+// planner's 256x256, 8-wave 128x128, 64x64 and 96x96 kernels); the others
+// take op(A) = A, op(B) = B only.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE,
           bool ALL_ORDERS>
 bool launch_orders(const DmaLaunch &d, hipStream_t stream) {
@@ -65,7 +65,7 @@ bool launch_dma_kernel(int kernel, const DmaLaunch &d, hipStream_t stream) {
     case GEMM_KERNEL_DMA32_64x64_S3:
       return launch_orders<32, 64, 64, 16, 2, 2, 3, 2, true>(d, stream);
     case GEMM_KERNEL_DMA16_96x96_S3:
-      return launch_orders<16, 96, 96, 32, 2, 2, 3, 2, false>(d, stream);
+      return launch_orders<16, 96, 96, 32, 2, 2, 3, 2, true>(d, stream);
   }
   return false;
 }

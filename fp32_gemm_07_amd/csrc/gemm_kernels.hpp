@@ -1117,14 +1117,17 @@ void mfma_dma_gemm_kernel(const float *__restrict__ A, const float *__restrict__
   // region rd_st, into slot ^ 1) two after each of the first MFMAs, then
   // (copy mode CM: 1 whole step, 2 range-checked) the LPW copies of step
   // cp_step into stage byte cp_stage one after every third MFMA from the
-  // group's second quarter on.
+  // group's second quarter on. The reads end within the group's first
+  // quarter, or its first half when both operands are read 4 bytes at a
+  // time (M- and N-contiguous panels: 12 reads each at 96 x 96), so the
+  // last of them has at least half a group of MFMAs to land.
   constexpr int kNm = 4 * FM * FN;
   constexpr int kNra = OpA::NREADS, kNr = kNra + OpB::NREADS;
   auto group_spread = [&](int slot, const float *rd_st, int rd_g, auto cm_c, int cp_step,
                           unsigned cp_stage) {
     constexpr int CM = decltype(cm_c)::value;
     constexpr int NC = CM ? LPW : 0;
-    static_assert(!kSpreadCopies || (kNr <= 2 * (kNm / 4) && kNm / 4 + 3 * LPW <= kNm),
+    static_assert(!kSpreadCopies || (kNr <= kNm && kNm / 4 + 3 * LPW <= kNm),
                   "side work fits the group");
     unroll_steps<0, kNm>([&](auto m_c) {
       constexpr int Mi = decltype(m_c)::value;

@@ -109,9 +109,8 @@ enum {
   GEMM_KERNEL_DMA32_64x64_S3 = 45,      /* mfma32, 64x64, K step 16, 4 waves, 3 stages */
   GEMM_KERNEL_DMA32_128x128_W8_S3 = 46, /* mfma32, 128x128, K step 16, 8 waves of 64x32, 3 stages */
   GEMM_KERNEL_DMA16_96x96_S3 = 47,      /* mfma16, 96x96, K step 32, 4 waves of 48x48, 3 stages;
-                                         * op(A) = A, op(B) = B only, and no register-staged
-                                         * counterpart: a plan whose copy offsets would pass
-                                         * 2^31 bytes is rejected */
+                                         * no register-staged counterpart: a plan whose copy
+                                         * offsets would pass 2^31 bytes is rejected */
   /* The optimisation ladder of the yekq.top LeetGPU walkthrough (sections v0
    * to v3; its v4 is GEMM_KERNEL_VALU_64x64), for comparison only. */
   GEMM_KERNEL_LADDER_V0 = 40,  /* one output per lane, lanes along rows (uncoalesced), 16x16 */

@@ -234,15 +234,17 @@ def test_general_large_tile_ragged(ta, tb):
 
 GENERAL_TAILS = [((1100, 777, 1000), 0, 0, (0, 0, 0)), ((1100, 777, 1000), 1, 0, (2, 3, 1)),
                  ((1100, 777, 1000), 0, 1, (0, 0, 4)), ((1100, 777, 1000), 1, 1, (1, 1, 2)),
-                 ((1792, 1792, 1792), 0, 0, (0, 0, 0)), ((1792, 1792, 1792), 0, 0, (3, 1, 2))]
+                 ((1792, 1792, 1792), 0, 0, (0, 0, 0)), ((1792, 1792, 1792), 0, 0, (3, 1, 2)),
+                 ((1792, 1792, 1792), 1, 0, (1, 2, 3)), ((1792, 1792, 1792), 0, 1, (0, 0, 0)),
+                 ((1792, 1792, 1792), 1, 1, (2, 0, 1))]
 
 
 @pytest.mark.parametrize("shape,ta,tb,pads", GENERAL_TAILS,
                          ids=[f"{m}x{k}x{n}-{'TN'[a]}{'TN'[b]}-{''.join(map(str, p))}"
                               for (m, k, n), a, b, p in GENERAL_TAILS])
 def test_general_split_tail(shape, ta, tb, pads):
-    """Shapes whose plans split only the last round of tiles (64 x 64 tiles in
-    every storage order, 96 x 96 for untransposed operands): the reduction of
+    """Shapes whose plans split only the last round of tiles (64 x 64 tiles at
+    1100 x 777 x 1000, 96 x 96 at 1792^3, each in every storage order): the reduction of
     the split tiles applies alpha, beta and ldc (row strides that are and are
     not multiples of 4), the whole tiles are stored directly; every output
     against the oracle."""
@@ -255,19 +257,46 @@ def test_general_split_tail(shape, ta, tb, pads):
     check(got, ref, S, M, N, ldc, "split tail general")
 
 
-@pytest.mark.parametrize("pads", [(0, 0, 0), (3, 1, 2)], ids=["dense", "padded"])
-def test_general_96_tiles(pads):
-    """1536^3: 16 x 16 tiles of 96 x 96, one per CU, none split (untransposed
-    operands): alpha, beta and row strides through the 96 x 96 kernel's own
-    stores; every output against the oracle."""
-    M = N = K = 1536
+# Shapes the planner gives 96 x 96 tiles, none split: 1536^3 (16 x 16 tiles,
+# one per CU), ragged M and N with K % 32 = 7 (1531 x 999 x 1529: rows of
+# A^T and B not 16-byte multiples) and a last K step of one element
+# (1529 x 4097 x 1531).
+TILES_96 = [((1536, 1536, 1536), (0, 0, 0)), ((1536, 1536, 1536), (3, 1, 2)),
+            ((1531, 999, 1529), (2, 3, 1)), ((1529, 4097, 1531), (1, 0, 3))]
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+@pytest.mark.parametrize("shape,pads", TILES_96,
+                         ids=[f"{m}x{k}x{n}-{''.join(map(str, p))}" for (m, k, n), p in TILES_96])
+def test_general_96_tiles(ta, tb, shape, pads):
+    """The 96 x 96 kernel (16 x 16 blocks; M- and N-contiguous operands
+    stored as 32-column panels, K-contiguous ones as swizzled rows) in every
+    storage order: alpha, beta and row strides through its own stores; every
+    output against the oracle."""
+    M, K, N = shape
     p = binding.gemm_f32_plan(M, N, K)
     assert binding.gemm_kernel_name(p.kernel) == "dma_mfma16_f32_96x96x32_w4_s3" and p.split_k == 1
-    say(f"general 96 x 96 tiles pads {pads}")
-    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=111)
+    say(f"general 96 x 96 tiles {'TN'[ta]}{'TN'[tb]} {M}x{K}x{N} pads {pads}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=111 + ta + 2 * tb + K)
     C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=112)[0]
-    got, ref, S, ldc = run_general(0, 0, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
-    check(got, ref, S, M, N, ldc, "96 x 96 general")
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.5, X, Y, -0.5, C0, pads=pads)
+    check(got, ref, S, M, N, ldc, f"96 x 96 general {ta}{tb} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+def test_general_96_tiles_integers_bit_exact(ta, tb):
+    """Small integers through the 96 x 96 kernel in every storage order
+    (1531 x 999 x 1529, alpha = 2, beta = -3): every value exact on both
+    sides, so the bits must match; pins which k each lane group reads from
+    the panels and swizzled rows."""
+    M, K, N = 1531, 999, 1529
+    p = binding.gemm_f32_plan(M, N, K)
+    assert binding.gemm_kernel_name(p.kernel) == "dma_mfma16_f32_96x96x32_w4_s3"
+    say(f"general 96 x 96 int {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "int", seed=120 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "int", seed=121)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 2.0, X, Y, -3.0, C0, pads=(1, 2, 3))
+    check(got, ref, S, M, N, ldc, f"96 x 96 int {ta}{tb}", bits=True)
 
 
 # A last K step of 1 to 4 elements in the planner's plans: the kernels with few
