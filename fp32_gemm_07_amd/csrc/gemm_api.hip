@@ -230,7 +230,7 @@ constexpr PlanCandidate kPlanCandidates[] = {
     {GEMM_KERNEL_DMA32_256x256_W8_S3, 0.966, 11.9, 5.6, 1, 0.966, 11.9, true, false, 0},
     {GEMM_KERNEL_DMA32_128x128_W8_S3, 0.982, 6.9, 3.9, 1, 0.982, 6.9, true, false, 0},
     {GEMM_KERNEL_DMA32_64x64_S3, 0.91, 1.2, 6.5, 2, 0.935, 1.2, true, true, 0},
-    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, false, true, 0},
+    {GEMM_KERNEL_DMA32_128x128_W4, 0.95, 7.0, 3.9, 2, 0.86, 2.0, true, true, 0},
     {GEMM_KERNEL_DMA16_96x96_S3, 0.95, 2.0, 4.0, 2, 0.97, 2.0, true, false, 64},
 };
 constexpr double kRateCuFlopPerUs = 256.0 * 2.38e3;   // FLOP per microsecond per CU

@@ -18,8 +18,7 @@ void launch_t(const DmaLaunch &d, hipStream_t stream) {
 }
 
 // ALL_ORDERS: the configuration is built for transposed operands too (the
-// planner's 256x256, 8-wave 128x128, 64x64 and 96x96 kernels); the others
-// take op(A) = A, op(B) = B only.
+// planner's five kernels); the others take op(A) = A, op(B) = B only.
 template <int MI, int BM, int BN, int BK, int WAVES_M, int WAVES_N, int NS, int WPE,
           bool ALL_ORDERS>
 bool launch_orders(const DmaLaunch &d, hipStream_t stream) {
@@ -47,7 +46,7 @@ bool launch_dma_kernel(int kernel, const DmaLaunch &d, hipStream_t stream) {
     case GEMM_KERNEL_DMA32_256x256_W8_S3:
       return launch_orders<32, 256, 256, 16, 2, 4, 3, 2, true>(d, stream);
     case GEMM_KERNEL_DMA32_128x128_W4:
-      return launch_orders<32, 128, 128, 16, 2, 2, 4, 2, false>(d, stream);
+      return launch_orders<32, 128, 128, 16, 2, 2, 4, 2, true>(d, stream);
     case GEMM_KERNEL_DMA16_128x128_W4:
       return launch_orders<16, 128, 128, 16, 2, 2, 4, 2, false>(d, stream);
     case GEMM_KERNEL_DMA16_64x64:

@@ -342,9 +342,8 @@ def test_general_short_last_step_integers_bit_exact(ta, tb, shape, kernel, split
                          ids=["NN", "NN-padded", "TN", "NT", "TT"])
 def test_general_short_k_large_output(ta, tb, pads):
     """4096 x 16 x 4096: the plain product's plan is the 4-wave 128 x 128
-    kernel (store-bound regime), which is built for op = identity only; the
-    general form takes it for untransposed operands (with alpha, beta and row
-    strides) and another kernel for transposed ones. Every output against the
+    kernel (store-bound regime); the general form takes it in every storage
+    order, with alpha, beta and row strides. Every output against the
     oracle."""
     M = N = 4096
     K = 16
