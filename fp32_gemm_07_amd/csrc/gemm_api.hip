@@ -163,11 +163,12 @@ Problem plain_problem(const float *A, const float *B, float *C, int M, int N, in
 // its first element: they must stay below 2^31 over the K range of one
 // workgroup. K-contiguous operand: about (BX*ld + k_span)*4 bytes;
 // M/N-contiguous: about (k_span*ld + BX)*4.
-constexpr long long kMaxOffset = 1LL << 31;
+// Counted in floats (bx <= 256, ld and k_span below 2^32: no overflow in
+// 64 bits), compared with 2^31 bytes / 4.
+constexpr long long kMaxOffsetFloats = (1LL << 31) / 4;
 bool operand_fits(bool kmajor, int bx, int ld, long long k_span) {
-  const long long bytes = kmajor ? 4 * ((long long)bx * ld + k_span)
-                                 : 4 * (k_span * ld + bx);
-  return bytes < kMaxOffset;
+  const long long floats = kmajor ? (long long)bx * ld + k_span : k_span * ld + bx;
+  return floats < kMaxOffsetFloats;
 }
 bool dma_fits(const Problem &p, int bm, int bn, int bk, int k_chunk) {
   const long long span = (long long)k_chunk + bk;
