@@ -355,6 +355,42 @@ def test_general_short_k_large_output(ta, tb, pads):
     check(got, ref, S, M, N, ldc, "short K general")
 
 
+# Short K over large ragged outputs, planned to the 4-wave 128 x 128 kernel:
+# edge tiles on both sides (M, N not multiples of 128), a K range shorter
+# than one step (15), one step and one element (17), one step and 15 (31).
+SHORT_K_RAGGED = [((4001, 17, 3999), (1, 2, 3)), ((3999, 15, 4001), (0, 0, 0)),
+                  ((4097, 31, 4095), (3, 1, 2))]
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+@pytest.mark.parametrize("shape,pads", SHORT_K_RAGGED,
+                         ids=[f"{m}x{k}x{n}" for (m, k, n), _ in SHORT_K_RAGGED])
+def test_general_short_k_ragged(ta, tb, shape, pads):
+    """The 4-wave 128 x 128 kernel in every storage order on ragged short-K
+    products, alpha and beta, padded rows: every output against the oracle."""
+    M, K, N = shape
+    assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_128x128_W4
+    say(f"general short K ragged {'TN'[ta]}{'TN'[tb]} {M}x{K}x{N}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=130 + K + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "uniform", seed=131)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 0.75, X, Y, 2.0, C0, pads=pads)
+    check(got, ref, S, M, N, ldc, f"short K ragged {ta}{tb} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
+def test_general_short_k_ragged_integers_bit_exact(ta, tb):
+    """Small integers through the 4-wave 128 x 128 kernel in every storage
+    order (4001 x 17 x 3999, alpha = 2, beta = -3): bit for bit, which pins
+    which k each lane reads from the transposed layouts and the zeroed tail."""
+    M, K, N = 4001, 17, 3999
+    assert binding.gemm_f32_plan(M, N, K).kernel == binding.GEMM_KERNEL_DMA32_128x128_W4
+    say(f"general short K ragged int {'TN'[ta]}{'TN'[tb]}")
+    X, Y = gemm_inputs.draw(M, K, N, "int", seed=140 + ta + 2 * tb)
+    C0 = gemm_inputs.draw(M, N, 1, "int", seed=141)[0]
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 2.0, X, Y, -3.0, C0, pads=(2, 1, 1))
+    check(got, ref, S, M, N, ldc, f"short K ragged int {ta}{tb}", bits=True)
+
+
 @pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
 def test_column_major_through_swapped_operands(ta, tb):
     """The column-major recipe of the header: A, B, C stored column-major
