@@ -18,9 +18,11 @@ from gpu_util import say, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
-# 1792^3: the plan splits only the last round of tiles (its own reduction).
+# 1792^3: the plan splits only the last round of tiles (its own reduction);
+# in the general form (op(A) = A^T) it is the 96 x 96 kernel's transposed
+# instantiation, and 4001 x 17 x 3999 the 4-wave 128 x 128 one's.
 CASES = [(1001, 513, 777, "plain"), (256, 8192, 256, "plain"), (1792, 1792, 1792, "plain"),
-         (300, 513, 260, "general")]
+         (300, 513, 260, "general"), (1792, 1792, 1792, "general"), (4001, 17, 3999, "general")]
 
 
 @pytest.mark.parametrize("M,K,N,form", CASES, ids=[f"{m}x{k}x{n}-{f}" for m, k, n, f in CASES])
