@@ -391,6 +391,49 @@ def test_general_short_k_ragged_integers_bit_exact(ta, tb):
     check(got, ref, S, M, N, ldc, f"short K ragged int {ta}{tb}", bits=True)
 
 
+# IEEE special values through the transposed layouts of the 96 x 96 kernel
+# (1531 x 999 x 1529) and the 4-wave 128 x 128 kernel (4001 x 17 x 3999):
+# every output is a sum of products over all of K, so neither the panels, the
+# swizzled rows, the zero fill of the edges nor the K tail may add a NaN or
+# hide one.
+SPECIAL_GENERAL = [((1531, 999, 1529), 700, 333, 901, 1000, [5, 1500]),
+                   ((4001, 17, 3999), 2100, 3, 16, 3001, [7, 4000])]
+
+
+@pytest.mark.parametrize("ta,tb", ORDERS[1:], ids=["TN", "NT", "TT"])
+@pytest.mark.parametrize("case", SPECIAL_GENERAL, ids=[f"{m}x{k}x{n}" for (m, k, n), *_ in SPECIAL_GENERAL])
+def test_general_special_values(ta, tb, case):
+    """A NaN at op(A)[i0, k0] makes row i0 NaN; a +Inf at op(B)[k1, j1] makes
+    column j1 +-Inf by the sign of op(A)[i, k1], NaN where that is 0; the
+    rest finite and within the bound of the oracle's general form."""
+    (M, K, N), i0, k0, k1, j1, zeros = case
+    assert binding.gemm_kernel_name(binding.gemm_f32_plan(M, N, K).kernel) in (
+        "dma_mfma16_f32_96x96x32_w4_s3", "dma_mfma32_f32_128x128x16_w4_s4")
+    say(f"general special values {'TN'[ta]}{'TN'[tb]} {M}x{K}x{N}")
+    X, Y = gemm_inputs.draw(M, K, N, "uniform", seed=150 + ta + 2 * tb)
+    X[i0, k0] = np.nan
+    Y[k1, j1] = np.inf
+    X[zeros, k1] = 0.0
+    C0 = np.full((M, N), np.nan, np.float32)
+    got, ref, S, ldc = run_general(ta, tb, M, N, K, 1.0, X, Y, 0.0, C0, pads=(1, 2, 3))
+    C = got.reshape(-1, ldc)[:M, :N]
+    want_nan = np.zeros((M, N), dtype=bool)
+    want_nan[i0, :] = True
+    want_nan[zeros, j1] = True
+    assert np.array_equal(np.isnan(C), want_nan), "NaN pattern"
+    rows = np.delete(np.arange(M), [i0, *zeros])
+    assert np.array_equal(C[rows, j1], np.where(X[rows, k1] > 0, np.inf, -np.inf).astype(np.float32))
+    R = ref.reshape(-1, ldc)[:M, :N]
+    assert np.array_equal(np.isnan(R), want_nan)
+    fin = np.isfinite(R)
+    fin[:, j1] = False
+    assert fin.sum() == (M - 1) * (N - 1)
+    assert np.isfinite(C[fin]).all()
+    err = np.abs(C[fin].astype(np.float64) - R[fin])
+    assert (err <= 1e-5 * S.reshape(M, N)[fin] + 1e-6).all(), f"worst {err.max()}"
+    assert np.isnan(got.reshape(-1, ldc)[:, N:]).all(), "padding of C written"
+
+
 @pytest.mark.parametrize("ta,tb", ORDERS, ids=["NN", "TN", "NT", "TT"])
 def test_column_major_through_swapped_operands(ta, tb):
     """The column-major recipe of the header: A, B, C stored column-major
